@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds no attention arithmetic: it only names the workload shapes
+and draws the random inputs, so that the GPU path and the CPU oracle see
+exactly the same numbers.
+
+Recipe (one stream per tensor and per (batch, head), so any head can be drawn
+on its own without drawing the whole problem):
+
+* generator: ``numpy.random.Generator(PCG64(SeedSequence([seed, t, b, h])))``
+  where ``t`` is 0, 1, 2, 3 for Q, K, V, dO;
+* values: ``standard_normal(float32)`` of shape (n, d), times the workload's
+  Q multiplier for Q (3 for the peaky-softmax workload), else 1;
+* rounding: for bf16 workloads the float32 values are rounded to bf16 with
+  round-to-nearest-even and kept as float32 (exactly representable), so the
+  oracle upcasts the very values the GPU receives.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "workload",
+    "round_to_bf16",
+    "draw_head",
+    "draw_inputs",
+    "pair_count",
+]
+
+TENSORS = ("q", "k", "v", "do")
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One problem shape: [B, H, n, d] tensors, element type, window."""
+
+    name: str
+    B: int
+    H: int
+    n: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    window: int = -1  # -1: no mask; w >= 0: |i - j| <= w
+    q_mult: float = 1.0
+    seed: int = 69000
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self):
+        return float(1.0 / np.sqrt(self.d))
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.n, self.d)
+
+
+WORKLOADS = [
+    Workload("single_head_f32_n256_d64", 1, 1, 256, 64, "f32", seed=69001,
+             note="single head, fp32, oracle-sized"),
+    Workload("bf16_b4h16_n2048_d64", 4, 16, 2048, 64, "bf16", seed=69002),
+    Workload("bf16_b2h32_n8192_d128_q3", 2, 32, 8192, 128, "bf16", q_mult=3.0,
+             seed=69003, note="Q scaled by 3: peaky softmax rows"),
+    Workload("bf16_b1h16_n32768_d128", 1, 16, 32768, 128, "bf16", seed=69004,
+             note="long context"),
+    Workload("bf16_b2h8_n16384_d256_w512", 2, 8, 16384, 256, "bf16", window=512,
+             seed=69005, note="Longformer-style local window |i-j|<=512"),
+]
+
+
+def workload(name_or_index):
+    """Look a workload up by name or by its position in ``WORKLOADS``."""
+    if isinstance(name_or_index, int):
+        return WORKLOADS[name_or_index]
+    for w in WORKLOADS:
+        if w.name == name_or_index:
+            return w
+    raise KeyError(name_or_index)
+
+
+def round_to_bf16(x):
+    """Round float32 values to the nearest bf16 (ties to even), as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+def _stream(seed, t, b, h):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, t, b, h])))
+
+
+def draw_head(wl, tensor, b, h, n=None, d=None):
+    """One (n, d) float32 slice of ``tensor`` ('q','k','v','do') at (b, h)."""
+    n = wl.n if n is None else n
+    d = wl.d if d is None else d
+    t = TENSORS.index(tensor)
+    x = _stream(wl.seed, t, b, h).standard_normal((n, d), dtype=np.float32)
+    if tensor == "q" and wl.q_mult != 1.0:
+        x *= np.float32(wl.q_mult)
+    if wl.dtype == "bf16":
+        x = round_to_bf16(x)
+    return x
+
+
+def draw_inputs(wl, tensors=TENSORS, heads=None):
+    """Dict of float32 arrays [B, H, n, d] (or [len(heads), n, d] if ``heads``
+    lists (b, h) pairs) for the requested tensors."""
+    out = {}
+    for name in tensors:
+        if heads is None:
+            arr = np.empty(wl.shape, dtype=np.float32)
+            for b in range(wl.B):
+                for h in range(wl.H):
+                    arr[b, h] = draw_head(wl, name, b, h)
+        else:
+            arr = np.stack([draw_head(wl, name, b, h) for (b, h) in heads])
+        out[name] = arr
+    return out
+
+
+def pair_count(n, window):
+    """Number of (query, key) pairs that take part: n*n without a window,
+    else the pairs with |i - j| <= window."""
+    if window < 0 or window >= n - 1:
+        return n * n
+    w = window
+    return n * (2 * w + 1) - w * (w + 1)
