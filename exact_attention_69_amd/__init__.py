@@ -1,0 +1,17 @@
+"""Exact scaled dot-product attention (forward + backward) for MI355X / gfx950.
+
+The compute path is libexattn.so (hand-written HIP kernels behind the C ABI in
+include/exattn.h); this package only marshals PyTorch device tensors into it.
+"""
+
+from ._binding import (  # noqa: F401
+    EXATTN_BF16,
+    EXATTN_F32,
+    ExattnError,
+    LIB_PATH,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
+    attn_fwd,
+    exattn_status_string,
+    load_library,
+)

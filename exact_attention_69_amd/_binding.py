@@ -1,0 +1,134 @@
+"""ctypes binding of libexattn.so: argument marshalling only.
+
+Every step of the attention path runs in the library's HIP kernels; this
+module checks tensor shapes/dtypes, allocates outputs with PyTorch (device
+memory only) and passes raw device pointers and the current HIP stream to the
+C entry points declared in include/exattn.h.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libexattn.so")
+
+EXATTN_F32 = 0
+EXATTN_BF16 = 1
+STATUS = {0: "EXATTN_OK", -1: "EXATTN_EINVAL", -2: "EXATTN_EUNSUPPORTED", -3: "EXATTN_EWORKSPACE", -4: "EXATTN_EHIP"}
+
+_lib = None
+
+
+class ExattnError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+def load_library(path=None):
+    """Load (once) and return the ctypes handle of libexattn.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_attention_69_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf, cs = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, cf, ci, vp, vp, vp]
+    lib.attn_fwd.restype = ci
+    lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.attn_bwd_workspace_bytes.restype = cs
+    lib.attn_bwd.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, vp, cs, vp]
+    lib.attn_bwd.restype = ci
+    lib.exattn_status_string.argtypes = [ci]
+    lib.exattn_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def exattn_status_string(status):
+    return load_library().exattn_status_string(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return EXATTN_BF16
+    if t.dtype == torch.float32:
+        return EXATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_inputs(*ts):
+    t0 = ts[0]
+    if t0.dim() != 4:
+        raise ValueError(f"expected [B, H, n, d] tensors, got shape {tuple(t0.shape)}")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.shape != t0.shape or t.dtype != t0.dtype:
+            raise ValueError("Q, K, V (and O, dO) must share shape and dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, n, d]")
+
+
+def _stream_ptr(t, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_fwd(q, k, v, scale=None, window=-1, out=None, lse=None, stream=None):
+    """Forward pass.  Returns (O, LSE): O like q, LSE float32 [B, H, n]."""
+    torch = _torch()
+    _check_inputs(q, k, v)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        st = load_library().attn_fwd(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     scale, int(window), out.data_ptr(), lse.data_ptr(), _stream_ptr(q, stream))
+    if st != 0:
+        raise ExattnError("attn_fwd", st, exattn_status_string(st))
+    return out, lse
+
+
+def attn_bwd_workspace_bytes(dtype_code, B, H, n, d):
+    return int(load_library().attn_bwd_workspace_bytes(dtype_code, B, H, n, d))
+
+
+def attn_bwd(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """Backward pass.  Returns (dQ, dK, dV), each like q."""
+    torch = _torch()
+    _check_inputs(q, k, v, o, do)
+    B, H, n, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, n]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(code, B, H, n, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    with torch.cuda.device(q.device):
+        st = load_library().attn_bwd(code, B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(),
+                                     dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream_ptr(q, stream))
+    if st != 0:
+        raise ExattnError("attn_bwd", st, exattn_status_string(st))
+    return dq, dk, dv

@@ -1,0 +1,389 @@
+// Backward attention kernels, bf16 inputs, fp32 accumulation, gfx950.
+//
+// The backward recomputes the probabilities from Q, K and the forward's
+// per-row log-sum-exp instead of reading a stored n x n matrix (the unite.ai
+// page "Flash Attention: Revolucionando a Eficiencia dos Modelos
+// Transformer", section "Entenda a Flash Attention", item 2; llmis.ru
+// chapter 3.1, section 5).  The gradient formulas are the chain rule of
+// O = softmax(scale Q K^T) V for the loss sum(O * dO):
+//   P = exp(scale*S - LSE), dV = P^T dO, dP = dO V^T, D = rowsum(dO * O),
+//   dS = P * (dP - D), dK = scale dS^T Q, dQ = scale dS K.
+//
+// Three launches, all stream ordered and deterministic (no atomics):
+//   1. rowdot: D for every query row (fp32 workspace).
+//   2. key side (KV-outer): a workgroup owns 32*NW keys, keeps their K and V
+//      rows in registers and accumulates dK, dV over the query tiles in the
+//      band; S and dP are computed with lanes indexed by key so that P and dS
+//      feed the dV/dK products straight from the accumulator registers.
+//   3. query side (Q-outer): a workgroup owns 32*NW query rows and
+//      accumulates dQ over the key tiles, recomputing S and dP with lanes
+//      indexed by query row.
+#include "bwd_common.hpp"
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace exattn {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Key side: dK, dV
+// ---------------------------------------------------------------------------
+template <int D>
+struct KvCfg {
+  static constexpr int NW = 4;   // waves; each owns 32 keys
+  static constexpr int BQ = 32;  // query rows per tile
+};
+
+template <int D, bool WINDOWED>
+__global__ __launch_bounds__(KvCfg<D>::NW * 64) void bwd_kv_bf16_kernel(
+    const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
+    const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
+    __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int n, int n_kblocks, int total_blocks, float scale,
+    float scale_log2, int window) {
+  constexpr int NW = KvCfg<D>::NW;
+  constexpr int BQ = KvCfg<D>::BQ;
+  constexpr int NT = NW * 64;
+  constexpr int BKV = 32 * NW;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  static_assert(BQ == 32, "one 32-row query block per tile");
+
+  __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BQ * D];  // [buf][Q/dO]
+  __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE*log2e / D]
+
+  const int bid = xcd_remap(blockIdx.x, total_blocks);
+  const int head = bid / n_kblocks;
+  const int kblk = bid - head * n_kblocks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+
+  const size_t hoff = (size_t)head * n * D;
+  const __bf16* Q = Qg + hoff;
+  const __bf16* dO = dOg + hoff;
+  const float* lse = LSEg + (size_t)head * n;
+  const float* dl = Dg + (size_t)head * n;
+
+  const int kb0 = kblk * BKV;
+  const int my_key = kb0 + wave * 32 + l32;
+
+  // K and V rows of this lane's key, as MFMA B operands (k along d).
+  bf16x8 kreg[NDS], vreg[NDS];
+  {
+    const bool ok = my_key < n;
+    const size_t off = hoff + (size_t)(ok ? my_key : 0) * D + 8 * hi;
+    const u32x4* ks = (const u32x4*)(Kg + off);
+    const u32x4* vs = (const u32x4*)(Vg + off);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      kreg[ds] = __builtin_bit_cast(bf16x8, ok ? ks[2 * ds] : u32x4{0, 0, 0, 0});
+      vreg[ds] = __builtin_bit_cast(bf16x8, ok ? vs[2 * ds] : u32x4{0, 0, 0, 0});
+    }
+  }
+
+  int q_lo = 0, q_hi = n;
+  if constexpr (WINDOWED) band_keys(kb0, kb0 + BKV, n, window, &q_lo, &q_hi);
+  const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
+  // query rows that see this lane's key (the window is symmetric)
+  int row_lo = 0, row_hi = n;
+  if constexpr (WINDOWED) band_keys(my_key, my_key + 1, n, window, &row_lo, &row_hi);
+  const unsigned row_span = (unsigned)max(row_hi - row_lo, 0);
+
+  TileCopy<D, BQ, NT> qcp, gcp;
+  float st_val = 0.0f;  // staged row statistic (threads < 2*BQ)
+  auto load_tile = [&](int t) {
+    const int i0 = t * BQ;
+    qcp.load(Q + (size_t)i0 * D, n - i0, tid);
+    gcp.load(dO + (size_t)i0 * D, n - i0, tid);
+    if (tid < 2 * BQ) {
+      const int r = tid & (BQ - 1), i = i0 + r;
+      if (tid < BQ)  // rows past the end get +inf so that P = 0 there
+        st_val = i < n ? lse[i] * kLog2e : __builtin_huge_valf();
+      else
+        st_val = i < n ? dl[i] : 0.0f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    qcp.store(tiles[buf][0], tid);
+    gcp.store(tiles[buf][1], tid);
+    if (tid < 2 * BQ) rowst[buf][tid / BQ][tid & (BQ - 1)] = st_val;
+  };
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  if (t_lo < t_hi) {
+    load_tile(t_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    const bool has_next = t + 1 < t_hi;
+    if (has_next) load_tile(t + 1);
+    const __bf16* Qs = tiles[buf][0];
+    const __bf16* dOs = tiles[buf][1];
+    const int i0 = t * BQ;
+
+    // S = Q K^T and dP = dO V^T, lanes indexed by key, registers by query row.
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      s = mfma32(lds_row_frag<D>(Qs, l32, ds, hi), kreg[ds], s);
+      dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), vreg[ds], dp);
+    }
+
+    bool need_mask = false;
+    if constexpr (WINDOWED) {
+      const int k_lo_w = kb0 + wave * 32;
+      need_mask = max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int rb = 8 * g + 4 * hi;  // rows rb .. rb+3 of the tile
+      const f32x4 l4 = *(const f32x4*)(&rowst[buf][0][rb]);
+      const f32x4 d4 = *(const f32x4*)(&rowst[buf][1][rb]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j]));
+        if constexpr (WINDOWED) {
+          // queries that see this lane's key: [row_lo, row_lo + row_span)
+          if (need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
+        }
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS, k along the tile's query rows.
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 pb = acc_to_operand(s, half);
+      const bf16x8 sb = acc_to_operand(dp, half);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = mfma32(lds_col_frag<D>(dOs, 16 * half, 32 * db, lane), pb, dv[db]);
+        dk[db] = mfma32(lds_col_frag<D>(Qs, 16 * half, 32 * db, lane), sb, dk[db]);
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (my_key < n) {
+    __bf16* dkr = dKg + hoff + (size_t)my_key * D;
+    __bf16* dvr = dVg + hoff + (size_t)my_key * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hi;
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale);
+        wk[1] = pack_bf16x2(dk[db][4 * g + 2] * scale, dk[db][4 * g + 3] * scale);
+        wv[0] = pack_bf16x2(dv[db][4 * g], dv[db][4 * g + 1]);
+        wv[1] = pack_bf16x2(dv[db][4 * g + 2], dv[db][4 * g + 3]);
+        *(u32x2*)(dkr + dd) = wk;
+        *(u32x2*)(dvr + dd) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query side: dQ
+// ---------------------------------------------------------------------------
+template <int D>
+struct QCfg;
+template <>
+struct QCfg<64> {
+  static constexpr int NW = 4, BC = 64;
+};
+template <>
+struct QCfg<128> {
+  static constexpr int NW = 4, BC = 32;
+};
+template <>
+struct QCfg<256> {
+  static constexpr int NW = 4, BC = 32;
+};
+
+template <int D, bool WINDOWED>
+__global__ __launch_bounds__(QCfg<D>::NW * 64) void bwd_q_bf16_kernel(
+    const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
+    const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
+    __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window) {
+  constexpr int NW = QCfg<D>::NW;
+  constexpr int BC = QCfg<D>::BC;
+  constexpr int NT = NW * 64;
+  constexpr int BR = 32 * NW;
+  constexpr int NKB = BC / 32;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+
+  __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BC * D];  // [buf][K/V]
+
+  const int bid = xcd_remap(blockIdx.x, total_blocks);
+  const int head = bid / n_qblocks;
+  const int qb = bid - head * n_qblocks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+
+  const size_t hoff = (size_t)head * n * D;
+  const __bf16* K = Kg + hoff;
+  const __bf16* V = Vg + hoff;
+  const int q0 = qb * BR;
+  const int my_row = q0 + wave * 32 + l32;
+
+  bf16x8 qreg[NDS], greg[NDS];
+  float lse2, dl;
+  {
+    const bool ok = my_row < n;
+    const size_t off = hoff + (size_t)(ok ? my_row : 0) * D + 8 * hi;
+    const u32x4* qs = (const u32x4*)(Qg + off);
+    const u32x4* gs = (const u32x4*)(dOg + off);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      qreg[ds] = __builtin_bit_cast(bf16x8, ok ? qs[2 * ds] : u32x4{0, 0, 0, 0});
+      greg[ds] = __builtin_bit_cast(bf16x8, ok ? gs[2 * ds] : u32x4{0, 0, 0, 0});
+    }
+    lse2 = ok ? LSEg[(size_t)head * n + my_row] * kLog2e : __builtin_huge_valf();
+    dl = ok ? Dg[(size_t)head * n + my_row] : 0.0f;
+  }
+
+  int k_lo = 0, k_hi = n;
+  if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
+  const int t_lo = k_lo / BC, t_hi = (k_hi + BC - 1) / BC;
+  // keys visible to this lane's row
+  int key_lo = 0, key_hi = n;
+  if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
+  const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
+
+  TileCopy<D, BC, NT> kcp, vcp;
+  auto load_tile = [&](int t) {
+    const int kbase = t * BC;
+    kcp.load(K + (size_t)kbase * D, n - kbase, tid);
+    vcp.load(V + (size_t)kbase * D, n - kbase, tid);
+  };
+  auto store_tile = [&](int buf) {
+    kcp.store(tiles[buf][0], tid);
+    vcp.store(tiles[buf][1], tid);
+  };
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
+
+  if (t_lo < t_hi) {
+    load_tile(t_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    const bool has_next = t + 1 < t_hi;
+    if (has_next) load_tile(t + 1);
+    const __bf16* Ks = tiles[buf][0];
+    const __bf16* Vs = tiles[buf][1];
+    const int kbase = t * BC;
+
+    // S^T = K Q^T and dP^T = V dO^T: lanes indexed by query row.
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
+        dp[kb] = mfma32(lds_row_frag<D>(Vs, kb * 32 + l32, ds, hi), greg[ds], dp[kb]);
+      }
+    }
+
+    bool need_mask = kbase + BC > n;
+    if constexpr (WINDOWED) {
+      const int r_lo = q0 + wave * 32;
+      need_mask = need_mask || max(r_lo + 31 - kbase, kbase + BC - 1 - r_lo) > window;
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
+        if (need_mask) {
+          const int key = kbase + kb * 32 + acc_row(r, lane);
+          p = (unsigned)(key - key_lo) < key_span ? p : 0.0f;
+        }
+        dp[kb][r] = p * (dp[kb][r] - dl);  // dS^T (unscaled)
+      }
+
+    // dQ^T += K^T dS^T, k along the tile's keys.
+#pragma unroll
+    for (int st = 0; st < BC / 16; ++st) {
+      const bf16x8 sb = acc_to_operand(dp[st >> 1], st & 1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(lds_col_frag<D>(Ks, 16 * st, 32 * db, lane), sb, dq[db]);
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (my_row < n) {
+    __bf16* dqr = dQg + hoff + (size_t)my_row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hi;
+        u32x2 w;
+        w[0] = pack_bf16x2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
+        w[1] = pack_bf16x2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+        *(u32x2*)(dqr + dd) = w;
+      }
+  }
+}
+
+template <int D, bool W>
+hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
+  const float scale_log2 = p.scale * kLog2e;
+  const long heads = (long)p.B * p.H;
+  hipError_t e = launch_rowdot<__bf16>((const __bf16*)p.o, (const __bf16*)p.dout, p.delta, heads * p.n, D, stream);
+  if (e != hipSuccess) return e;
+
+  constexpr int BKV = 32 * KvCfg<D>::NW;
+  const int nkb = (p.n + BKV - 1) / BKV;
+  const long tk = (long)nkb * heads;
+  constexpr int BR = 32 * QCfg<D>::NW;
+  const int nqb = (p.n + BR - 1) / BR;
+  const long tq = (long)nqb * heads;
+  if (tk > 0x7fffffffL || tq > 0x7fffffffL) return hipErrorInvalidValue;
+
+  hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(KvCfg<D>::NW * 64), 0, stream,
+                     (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
+                     p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(QCfg<D>::NW * 64), 0, stream,
+                     (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
+                     p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  const bool w = p.window >= 0;
+  switch (p.d) {
+    case 64: return w ? bwd_d<64, true>(p, stream) : bwd_d<64, false>(p, stream);
+    case 128: return w ? bwd_d<128, true>(p, stream) : bwd_d<128, false>(p, stream);
+    case 256: return w ? bwd_d<256, true>(p, stream) : bwd_d<256, false>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace exattn

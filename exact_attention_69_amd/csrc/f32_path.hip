@@ -1,0 +1,311 @@
+// fp32 forward and backward kernels (vector ALU, fp32 throughout).
+//
+// The fp32 element type is the accuracy path: scores, probabilities and
+// gradients stay in fp32 with no bf16 rounding.  It follows the same scheme
+// as the bf16 path -- key/value tiles staged in LDS, an online softmax with a
+// running max and sum in the forward (llmis.ru chapter 3.1, section 5), and
+// a backward that recomputes P from the saved log-sum-exp (the unite.ai
+// Flash Attention page, "Entenda a Flash Attention", item 2) -- but on the
+// vector ALU: a row of d values is split over TPR = 8 lanes, each holding
+// d/8 of them, and dot products are finished with xor shuffles.
+#include <math.h>
+
+#include "bwd_common.hpp"
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace exattn {
+namespace {
+
+constexpr int TPR = 8;          // lanes per row
+constexpr int ROWS = 256 / TPR; // rows per 256-thread block
+// rows per staged LDS tile (two tiles of TK x D floats must fit in 64 KiB)
+template <int D>
+constexpr int tile_rows() { return D == 256 ? 16 : 32; }
+
+__device__ __forceinline__ float row_sum8(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  return x;
+}
+
+// Element e of this lane's slice of a row is column TPR*e + sub, so the 8
+// lanes of a row read 8 consecutive floats (conflict-free LDS access).
+
+// ----------------------------------------------------------------------------
+// Forward: block = 32 query rows; loops over 32-key tiles.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
+                                                      const float* __restrict__ Vg, float* __restrict__ Og,
+                                                      float* __restrict__ LSEg, int n, int nqb, float scale,
+                                                      int window) {
+  constexpr int E = D / TPR;
+  constexpr int TK = tile_rows<D>();
+  __shared__ float Ks[TK][D];
+  __shared__ float Vs[TK][D];
+  const int head = blockIdx.x / nqb, qb = blockIdx.x - (blockIdx.x / nqb) * nqb;
+  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
+  const int row = qb * ROWS + rloc;
+  const size_t hoff = (size_t)head * n * D;
+  const float* K = Kg + hoff;
+  const float* V = Vg + hoff;
+
+  float q[E], acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    q[e] = row < n ? Qg[hoff + (size_t)row * D + TPR * e + sub] : 0.0f;
+    acc[e] = 0.0f;
+  }
+  float m = -INFINITY, l = 0.0f;
+
+  int k_lo = 0, k_hi = n;
+  if (window >= 0) band_keys(qb * ROWS, qb * ROWS + ROWS, n, window, &k_lo, &k_hi);
+  // keys visible to this row: [key_lo, key_lo + key_span)
+  int key_lo = 0, key_hi = n;
+  band_keys(row, row + 1, n, window, &key_lo, &key_hi);
+  const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
+  for (int k0 = (k_lo / TK) * TK; k0 < k_hi; k0 += TK) {
+    __syncthreads();
+    for (int i = tid; i < TK * D; i += 256) {
+      const int r = i / D, c = i - (i / D) * D;
+      const bool ok = k0 + r < n;
+      Ks[r][c] = ok ? K[(size_t)(k0 + r) * D + c] : 0.0f;
+      Vs[r][c] = ok ? V[(size_t)(k0 + r) * D + c] : 0.0f;
+    }
+    __syncthreads();
+    float s[TK];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part = fmaf(q[e], Ks[j][TPR * e + sub], part);
+      float sj = row_sum8(part) * scale;
+      sj = (unsigned)(k0 + j - key_lo) < key_span ? sj : -INFINITY;
+      s[j] = sj;
+      mx = fmaxf(mx, sj);
+    }
+    const float m_new = fmaxf(m, mx);
+    const float msub = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = expf(m - msub);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      const float p = expf(s[j] - msub);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(p, Vs[j][TPR * e + sub], acc[e]);
+    }
+    m = m_new;
+  }
+  if (row < n) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < E; ++e) Og[hoff + (size_t)row * D + TPR * e + sub] = acc[e] * inv;
+    if (sub == 0) LSEg[(size_t)head * n + row] = m + logf(l);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Backward, key side: block = 32 keys; accumulates dK and dV over query tiles.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
+                                                         const float* __restrict__ Vg, const float* __restrict__ dOg,
+                                                         const float* __restrict__ LSEg, const float* __restrict__ Dg,
+                                                         float* __restrict__ dKg, float* __restrict__ dVg, int n,
+                                                         int nkb, float scale, int window) {
+  constexpr int E = D / TPR;
+  constexpr int TK = tile_rows<D>();
+  __shared__ float Qs[TK][D];
+  __shared__ float dOs[TK][D];
+  __shared__ float Ls[TK], Ds[TK];
+  const int head = blockIdx.x / nkb, kb = blockIdx.x - (blockIdx.x / nkb) * nkb;
+  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
+  const int key = kb * ROWS + rloc;
+  const size_t hoff = (size_t)head * n * D;
+  const float* Q = Qg + hoff;
+  const float* dO = dOg + hoff;
+  const float* lse = LSEg + (size_t)head * n;
+  const float* dl = Dg + (size_t)head * n;
+
+  float k[E], v[E], dk[E], dv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    k[e] = key < n ? Kg[hoff + (size_t)key * D + TPR * e + sub] : 0.0f;
+    v[e] = key < n ? Vg[hoff + (size_t)key * D + TPR * e + sub] : 0.0f;
+    dk[e] = 0.0f;
+    dv[e] = 0.0f;
+  }
+  // queries that can see any key of this block
+  int q_lo = 0, q_hi = n;
+  if (window >= 0) band_keys(kb * ROWS, kb * ROWS + ROWS, n, window, &q_lo, &q_hi);
+  // query rows that see this key: [row_lo, row_lo + row_span); none if key >= n
+  int row_lo = 0, row_hi = n;
+  band_keys(key, key + 1, n, window, &row_lo, &row_hi);
+  const unsigned row_span = key < n ? (unsigned)max(row_hi - row_lo, 0) : 0u;
+  for (int i0 = (q_lo / TK) * TK; i0 < q_hi; i0 += TK) {
+    __syncthreads();
+    for (int i = tid; i < TK * D; i += 256) {
+      const int r = i / D, c = i - (i / D) * D;
+      const bool ok = i0 + r < n;
+      Qs[r][c] = ok ? Q[(size_t)(i0 + r) * D + c] : 0.0f;
+      dOs[r][c] = ok ? dO[(size_t)(i0 + r) * D + c] : 0.0f;
+    }
+    if (tid < TK) {
+      const bool ok = i0 + tid < n;
+      Ls[tid] = ok ? lse[i0 + tid] : 0.0f;
+      Ds[tid] = ok ? dl[i0 + tid] : 0.0f;
+    }
+    __syncthreads();
+    for (int r = 0; r < TK; ++r) {
+      const int qi = i0 + r;
+      float ps = 0.0f, pd = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ps = fmaf(k[e], Qs[r][TPR * e + sub], ps);
+        pd = fmaf(v[e], dOs[r][TPR * e + sub], pd);
+      }
+      const float sc = row_sum8(ps) * scale;
+      const float dp = row_sum8(pd);
+      const bool live = (unsigned)(qi - row_lo) < row_span;
+      const float p = live ? expf(sc - Ls[r]) : 0.0f;
+      const float ds = p * (dp - Ds[r]) * scale;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dv[e] = fmaf(p, dOs[r][TPR * e + sub], dv[e]);
+        dk[e] = fmaf(ds, Qs[r][TPR * e + sub], dk[e]);
+      }
+    }
+  }
+  if (key < n) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      dKg[hoff + (size_t)key * D + TPR * e + sub] = dk[e];
+      dVg[hoff + (size_t)key * D + TPR * e + sub] = dv[e];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Backward, query side: block = 32 query rows; accumulates dQ over key tiles.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
+                                                        const float* __restrict__ Vg, const float* __restrict__ dOg,
+                                                        const float* __restrict__ LSEg, const float* __restrict__ Dg,
+                                                        float* __restrict__ dQg, int n, int nqb, float scale,
+                                                        int window) {
+  constexpr int E = D / TPR;
+  constexpr int TK = tile_rows<D>();
+  __shared__ float Ks[TK][D];
+  __shared__ float Vs[TK][D];
+  const int head = blockIdx.x / nqb, qb = blockIdx.x - (blockIdx.x / nqb) * nqb;
+  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
+  const int row = qb * ROWS + rloc;
+  const size_t hoff = (size_t)head * n * D;
+  const float* K = Kg + hoff;
+  const float* V = Vg + hoff;
+
+  float q[E], g[E], dq[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    q[e] = row < n ? Qg[hoff + (size_t)row * D + TPR * e + sub] : 0.0f;
+    g[e] = row < n ? dOg[hoff + (size_t)row * D + TPR * e + sub] : 0.0f;
+    dq[e] = 0.0f;
+  }
+  const float lse = row < n ? LSEg[(size_t)head * n + row] : 0.0f;
+  const float dl = row < n ? Dg[(size_t)head * n + row] : 0.0f;
+
+  int k_lo = 0, k_hi = n;
+  if (window >= 0) band_keys(qb * ROWS, qb * ROWS + ROWS, n, window, &k_lo, &k_hi);
+  // keys visible to this row: [key_lo, key_lo + key_span); none if row >= n
+  int key_lo = 0, key_hi = n;
+  band_keys(row, row + 1, n, window, &key_lo, &key_hi);
+  const unsigned key_span = row < n ? (unsigned)max(key_hi - key_lo, 0) : 0u;
+  for (int k0 = (k_lo / TK) * TK; k0 < k_hi; k0 += TK) {
+    __syncthreads();
+    for (int i = tid; i < TK * D; i += 256) {
+      const int r = i / D, c = i - (i / D) * D;
+      const bool ok = k0 + r < n;
+      Ks[r][c] = ok ? K[(size_t)(k0 + r) * D + c] : 0.0f;
+      Vs[r][c] = ok ? V[(size_t)(k0 + r) * D + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int j = 0; j < TK; ++j) {
+      const int key = k0 + j;
+      float ps = 0.0f, pd = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ps = fmaf(q[e], Ks[j][TPR * e + sub], ps);
+        pd = fmaf(g[e], Vs[j][TPR * e + sub], pd);
+      }
+      const float sc = row_sum8(ps) * scale;
+      const float dp = row_sum8(pd);
+      const bool live = (unsigned)(key - key_lo) < key_span;
+      const float p = live ? expf(sc - lse) : 0.0f;
+      const float ds = p * (dp - dl) * scale;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dq[e] = fmaf(ds, Ks[j][TPR * e + sub], dq[e]);
+    }
+  }
+  if (row < n) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) dQg[hoff + (size_t)row * D + TPR * e + sub] = dq[e];
+  }
+}
+
+template <int D>
+hipError_t fwd_d(const FwdParams& p, hipStream_t stream) {
+  const int nqb = (p.n + ROWS - 1) / ROWS;
+  const long total = (long)nqb * p.B * p.H;
+  if (total > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
+                     (const float*)p.k, (const float*)p.v, (float*)p.o, p.lse, p.n, nqb, p.scale, p.window);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
+  const int nb = (p.n + ROWS - 1) / ROWS;
+  const long total = (long)nb * p.B * p.H;
+  if (total > 0x7fffffffL) return hipErrorInvalidValue;
+  hipError_t e = launch_rowdot<float>((const float*)p.o, (const float*)p.dout, p.delta, (long)p.B * p.H * p.n, D,
+                                      stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_kv_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
+                     (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dk,
+                     (float*)p.dv, p.n, nb, p.scale, p.window);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_q_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
+                     (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dq, p.n,
+                     nb, p.scale, p.window);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return fwd_d<64>(p, stream);
+    case 128: return fwd_d<128>(p, stream);
+    case 256: return fwd_d<256>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return bwd_d<64>(p, stream);
+    case 128: return bwd_d<128>(p, stream);
+    case 256: return bwd_d<256>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace exattn

@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exattn {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, n, d;
+  float scale;
+  int window;  // -1: no mask
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: [B, H, n] fp32, D = rowsum(dO * O)
+  int B, H, n, d;
+  float scale;
+  int window;
+};
+
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
+
+// Band of the sliding window, used to skip tiles (host and device).
+// Keys [lo, hi) that any row in [r0, r1) may attend to.
+__host__ __device__ inline void band_keys(int r0, int r1, int n, int window, int* lo, int* hi) {
+  if (window < 0) {
+    *lo = 0;
+    *hi = n;
+    return;
+  }
+  long a = (long)r0 - window, b = (long)r1 - 1 + window + 1;
+  *lo = a < 0 ? 0 : (int)a;
+  *hi = b > n ? n : (int)b;
+}
+
+}  // namespace exattn

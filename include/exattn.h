@@ -1,0 +1,133 @@
+/*
+ * exattn.h -- C ABI of the exact scaled dot-product attention library
+ * (forward and backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed
+ *   For every (batch b, head h), with Q, K, V, O, dO the (n, d) slices at
+ *   (b, h):
+ *     S   = scale * Q K^T                     (n x n, never stored)
+ *     P   = row-softmax(S) over the keys each row may see
+ *     O   = P V
+ *     LSE = per-row natural log of sum_j exp(S_ij)
+ *   and, for the backward, the gradients of L = sum(O * dO):
+ *     dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   The forward is the scaled dot-product attention of the llmis.ru chapter
+ *   3.1 "The cost of attention", section 2; it is evaluated tile by tile with
+ *   an online softmax (running row max and row sum, section 5 of the same
+ *   chapter), so the n x n matrices S and P are never written to device
+ *   memory.  The backward recomputes P from Q, K and the saved LSE instead of
+ *   storing it (the unite.ai page "Flash Attention: Revolucionando a
+ *   Eficiencia dos Modelos Transformer", section "Entenda a Flash Attention",
+ *   item 2); its formulas are the chain rule of the forward definition.
+ *
+ * Sliding window
+ *   window < 0 : every query row sees every key (no mask).
+ *   window >= 0: row i sees keys j with |i - j| <= window (the Longformer
+ *                local pattern of the llmis.ru chapter's section 3, read as
+ *                symmetric and inclusive).  Key tiles that lie wholly outside
+ *                a query tile's band are skipped, not computed.
+ *
+ * Layout and types (all tensors are DEVICE pointers)
+ *   Q, K, V, O, dO, dQ, dK, dV : contiguous row-major [B, H, n, d]; element
+ *                                type `dtype` (EXATTN_F32 = float,
+ *                                EXATTN_BF16 = bfloat16 bit patterns).
+ *   LSE                        : contiguous [B, H, n], float32, natural log.
+ *   workspace                  : device scratch owned by the caller, at least
+ *                                attn_bwd_workspace_bytes() bytes.
+ *   Arithmetic: bf16 operands with fp32 accumulation and fp32 softmax
+ *   statistics; probabilities and dS are rounded to bf16 before the matrix
+ *   products that consume them.  The f32 type computes in fp32 throughout.
+ *   Supported head dims d: 64, 128, 256.  Any n >= 1 (ragged tails masked).
+ *
+ * Ownership and execution
+ *   The caller allocates and owns every buffer; the library allocates nothing
+ *   and keeps no pointer after a call returns.  Inputs are read only; outputs
+ *   are completely overwritten (no need to clear them).  Every call only
+ *   enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *   returns without synchronising; a device fault surfaces at the caller's
+ *   next synchronisation.  Calls are reentrant; two calls that share an
+ *   output or workspace buffer must be ordered by the caller.
+ *
+ * Errors (no exception crosses the ABI; nothing is launched on error)
+ *   EXATTN_EINVAL       null pointer, B/H/n < 1, window < -1, non-finite or
+ *                       non-positive scale, a pointer not 16-byte aligned,
+ *                       an output buffer overlapping an input buffer, or a
+ *                       problem of 2^31 elements or more per tensor.
+ *   EXATTN_EUNSUPPORTED d not in {64, 128, 256}, or an unknown dtype.
+ *   EXATTN_EWORKSPACE   workspace smaller than attn_bwd_workspace_bytes().
+ *   EXATTN_EHIP         the HIP runtime reported an error at launch.
+ */
+#ifndef EXATTN_H
+#define EXATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { EXATTN_F32 = 0, EXATTN_BF16 = 1 } exattn_dtype;
+
+typedef enum {
+  EXATTN_OK = 0,
+  EXATTN_EINVAL = -1,
+  EXATTN_EUNSUPPORTED = -2,
+  EXATTN_EWORKSPACE = -3,
+  EXATTN_EHIP = -4
+} exattn_status;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T) V and LSE, per (b, h).
+ *   dtype  : EXATTN_F32 or EXATTN_BF16 (type of Q, K, V and O).
+ *   B, H, n, d : batch, heads, sequence length, head dim.
+ *   Q, K, V: inputs [B, H, n, d].
+ *   scale  : multiplier of Q K^T (normally 1/sqrt(d)); finite, > 0.
+ *   window : -1 for full attention, else the half-width w of |i - j| <= w.
+ *   O      : output [B, H, n, d], same dtype as the inputs.
+ *   LSE    : output [B, H, n] float32, m_i + ln(l_i) per row.
+ *   stream : hipStream_t to enqueue on.
+ * Returns an exattn_status.
+ */
+int attn_fwd(int dtype, int B, int H, int n, int d,
+             const void *Q, const void *K, const void *V,
+             float scale, int window,
+             void *O, float *LSE,
+             void *stream);
+
+/*
+ * Bytes of device workspace that attn_bwd needs for this problem (the fp32
+ * row statistic D = rowsum(dO * O), [B, H, n]).  Returns 0 for arguments that
+ * attn_bwd would reject.
+ */
+size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d);
+
+/*
+ * Backward pass: gradients of sum(O * dO) with respect to Q, K and V.
+ *   Q, K, V : the forward's inputs; O and LSE: the forward's outputs for
+ *             exactly these inputs, scale and window (P is recomputed from
+ *             them, so a mismatched O or LSE gives wrong gradients).
+ *   dO      : upstream gradient [B, H, n, d], same dtype.
+ *   dQ, dK, dV : outputs [B, H, n, d], same dtype; fully overwritten.
+ *   workspace, workspace_bytes : caller-owned device scratch, at least
+ *             attn_bwd_workspace_bytes(); its contents on entry are ignored
+ *             and on return are unspecified.
+ *   stream  : hipStream_t to enqueue on.
+ * Returns an exattn_status.
+ */
+int attn_bwd(int dtype, int B, int H, int n, int d,
+             const void *Q, const void *K, const void *V,
+             const void *O, const void *dO, const float *LSE,
+             float scale, int window,
+             void *dQ, void *dK, void *dV,
+             void *workspace, size_t workspace_bytes,
+             void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *exattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXATTN_H */
