@@ -1,0 +1,168 @@
+"""Benchmark: exact attention forward + backward on one MI355X.
+
+A step is one forward (attn_fwd) plus one backward (attn_bwd) over the whole
+batch of the n = 8192, d = 128 workload (B = 2, H = 32, bf16, Q scaled by 3),
+inputs resident in device memory.  Throughput counts the algorithmic FLOPs
+4*B*H*n^2*d (forward) + 10*B*H*n^2*d (backward), scaled by the fraction of
+(query, key) pairs a window lets through.
+
+Prints ONE JSON line.  Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--cpu-seconds S]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak at n=8192, d=128 (1 GPU)"
+DEFAULT_WORKLOAD = "bf16_b2h32_n8192_d128_q3"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(wl):
+    from workloads import pair_count
+    pairs = pair_count(wl.n, wl.window) * wl.B * wl.H
+    return 4.0 * pairs * wl.d, 10.0 * pairs * wl.d
+
+
+def hbm_bytes(wl):
+    """Algorithmic HBM bytes per call: fwd reads Q,K,V and writes O, LSE;
+    bwd reads Q,K,V,O,dO,LSE, writes dQ,dK,dV and writes+reads D."""
+    eb = 2 if wl.dtype == "bf16" else 4
+    t = wl.B * wl.H * wl.n * wl.d * eb
+    r = wl.B * wl.H * wl.n * 4
+    return 4 * t + r, 8 * t + 3 * r
+
+
+def cpu_baseline(wl, seconds):
+    """Time the fp64 oracle (as it stands) on whole heads of the workload
+    until about `seconds` of CPU work; report TFLOP/s on the same FLOP count."""
+    import numpy as np
+    import oracle
+    from workloads import draw_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    fwd_f, bwd_f = flops(wl)
+    per_head = (fwd_f + bwd_f) / (wl.B * wl.H)
+    done, t_total, heads = 0.0, 0.0, []
+    h = 0
+    while t_total < seconds and h < wl.B * wl.H:
+        b, hh = divmod(h, wl.H)
+        q, k, v, do = (draw_head(wl, x, b, hh) for x in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        oracle.attention_forward(q, k, v, wl.scale, wl.window)
+        oracle.attention_backward(q, k, v, do, wl.scale, wl.window)
+        t_total += time.perf_counter() - t0
+        done += per_head
+        heads.append((b, hh))
+        h += 1
+    return {"value": done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on {len(heads)} of {wl.B * wl.H} heads (b,h)={heads[0]}.."
+                      f"{heads[-1]}, {t_total:.1f} s, BLAS threads={threads}, host cpus={os.cpu_count()}"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the attention path runs on a single device); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_69_amd as ea
+    from workloads import draw_inputs, workload
+
+    wl = workload(args.workload)
+    fwd_f, bwd_f = flops(wl)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x = draw_inputs(wl)
+    t = {k: torch.from_numpy(v).to(dev, tdt) for k, v in x.items()}
+    del x
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    code = ea.EXATTN_BF16 if wl.dtype == "bf16" else ea.EXATTN_F32
+    ws = torch.empty(max(ea.attn_bwd_workspace_bytes(code, wl.B, wl.H, wl.n, wl.d), 256), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ea.attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream)
+        ea.attn_bwd(q, k, v, o, do, lse, wl.scale, wl.window, workspace=ws, dq=dq, dk=dk, dv=dv, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Whole steps, bracketed by device syncs, timed with events on the stream.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        ea.attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream)
+        ev[s][1].record(stream)
+        ea.attn_bwd(q, k, v, o, do, lse, wl.scale, wl.window, workspace=ws, dq=dq, dk=dk, dv=dv, stream=stream)
+        ev[s][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms = total_ms / args.steps
+    peak = PEAK_TFLOPS[wl.dtype]
+    value = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
+
+    # The forward is a single kernel launch per call, so its events time that
+    # kernel; its algorithmic FLOPs per launch are 4*B*H*pairs*d.
+    fwd_tflops = fwd_f / (fwd_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(fwd_tflops / peak, 4), "traffic": None,
+                "kernel": f"fwd_bf16_kernel<{wl.d}> (attn_fwd, one launch per call)",
+                "algorithmic_flops_per_launch": fwd_f, "avg_launch_ms": round(fwd_ms, 4)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "n": wl.n, "d": wl.d, "window": wl.window,
+                   "q_mult": wl.q_mult, "scale": wl.scale},
+        "pct_bf16_peak": round(100.0 * value / peak, 2),
+        "detail": {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                   "fwd_tflops": round(fwd_tflops, 2), "bwd_tflops": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 2),
+                   "flops_per_step": fwd_f + bwd_f, "wall_s_timed": round(wall, 3),
+                   "fwd_hbm_gbs_algorithmic": round(hbm_bytes(wl)[0] / (fwd_ms * 1e-3) / 1e9, 1),
+                   "bwd_hbm_gbs_algorithmic": round(hbm_bytes(wl)[1] / (bwd_ms * 1e-3) / 1e9, 1)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -11,8 +11,8 @@
 //
 // Three launches, all stream ordered and deterministic (no atomics):
 //   1. rowdot: D for every query row (fp32 workspace).
-//   2. key side (KV-outer): a workgroup owns 32*NW keys, keeps their K and V
-//      rows in registers and accumulates dK, dV over the query tiles in the
+//   2. key side (KV-outer): a workgroup owns 32*NW keys, keeps their K rows in
+//      registers and V rows in LDS, and accumulates dK, dV over the query tiles in the
 //      band; S and dP are computed with lanes indexed by key so that P and dS
 //      feed the dV/dK products straight from the accumulator registers.
 //   3. query side (Q-outer): a workgroup owns 32*NW query rows and
@@ -32,10 +32,11 @@ template <int D>
 struct KvCfg {
   static constexpr int NW = 4;   // waves; each owns 32 keys
   static constexpr int BQ = 32;  // query rows per tile
+  static constexpr int WPE = D == 256 ? 1 : 2;  // waves per SIMD
 };
 
 template <int D, bool WINDOWED>
-__global__ __launch_bounds__(KvCfg<D>::NW * 64) void bwd_kv_bf16_kernel(
+__global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int n, int n_kblocks, int total_blocks, float scale,
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64) void bwd_kv_bf16_kernel(
   static_assert(BQ == 32, "one 32-row query block per tile");
 
   __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BQ * D];  // [buf][Q/dO]
+  __shared__ __attribute__((aligned(16))) __bf16 vres[BKV * D];        // this block's V rows
   __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE*log2e / D]
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
@@ -65,18 +67,20 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64) void bwd_kv_bf16_kernel(
   const int kb0 = kblk * BKV;
   const int my_key = kb0 + wave * 32 + l32;
 
-  // K and V rows of this lane's key, as MFMA B operands (k along d).
-  bf16x8 kreg[NDS], vreg[NDS];
+  // K row of this lane's key as an MFMA B operand (k along d), in registers;
+  // the block's V rows (B operand of dP = dO V^T) stay resident in LDS.
+  bf16x8 kreg[NDS];
   {
     const bool ok = my_key < n;
     const size_t off = hoff + (size_t)(ok ? my_key : 0) * D + 8 * hi;
     const u32x4* ks = (const u32x4*)(Kg + off);
-    const u32x4* vs = (const u32x4*)(Vg + off);
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      kreg[ds] = __builtin_bit_cast(bf16x8, ok ? ks[2 * ds] : u32x4{0, 0, 0, 0});
-      vreg[ds] = __builtin_bit_cast(bf16x8, ok ? vs[2 * ds] : u32x4{0, 0, 0, 0});
-    }
+    for (int ds = 0; ds < NDS; ++ds) kreg[ds] = __builtin_bit_cast(bf16x8, ok ? ks[2 * ds] : u32x4{0, 0, 0, 0});
+  }
+  {
+    TileCopy<D, BKV, NT> vcp;
+    vcp.load(Vg + hoff + (size_t)kb0 * D, n - kb0, tid);
+    vcp.store(vres, tid);  // visible after the first barrier below
   }
 
   int q_lo = 0, q_hi = n;
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64) void bwd_kv_bf16_kernel(
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       s = mfma32(lds_row_frag<D>(Qs, l32, ds, hi), kreg[ds], s);
-      dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), vreg[ds], dp);
+      dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), lds_row_frag<D>(vres, wave * 32 + l32, ds, hi), dp);
     }
 
     bool need_mask = false;

@@ -32,23 +32,25 @@ namespace {
 // normalisation uses the same max, so the result is unchanged.
 constexpr float kRescaleThreshold = 8.0f;
 
+// NW waves per workgroup (32 query rows each), BC keys per tile, WPE the
+// waves per SIMD the register budget is sized for.
 template <int D>
 struct FwdCfg;
 template <>
 struct FwdCfg<64> {
-  static constexpr int NW = 4, BC = 64;
+  static constexpr int NW = 4, BC = 64, WPE = 2;
 };
 template <>
 struct FwdCfg<128> {
-  static constexpr int NW = 4, BC = 64;
+  static constexpr int NW = 4, BC = 64, WPE = 2;
 };
 template <>
 struct FwdCfg<256> {
-  static constexpr int NW = 4, BC = 32;
+  static constexpr int NW = 4, BC = 32, WPE = 1;
 };
 
 template <int D, bool WINDOWED>
-__global__ __launch_bounds__(FwdCfg<D>::NW * 64) void fwd_bf16_kernel(
+__global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n_qblocks, int total_blocks,
     float scale_log2, int window) {
