@@ -77,11 +77,9 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) kreg[ds] = __builtin_bit_cast(bf16x8, ok ? ks[2 * ds] : u32x4{0, 0, 0, 0});
   }
-  {
-    TileCopy<D, BKV, NT> vcp;
-    vcp.load(Vg + hoff + (size_t)kb0 * D, n - kb0, tid);
-    vcp.store(vres, tid);  // visible after the first barrier below
-  }
+  // V rows of this block, resident in LDS (visible after the first barrier);
+  // key rows past n are clamped copies and only feed unstored dK/dV rows.
+  TileAsync<D, BKV, NT>::issue(Vg + hoff + (size_t)kb0 * D, n - kb0, vres, tid);
 
   int q_lo = 0, q_hi = n;
   if constexpr (WINDOWED) band_keys(kb0, kb0 + BKV, n, window, &q_lo, &q_hi);
@@ -91,12 +89,14 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   if constexpr (WINDOWED) band_keys(my_key, my_key + 1, n, window, &row_lo, &row_hi);
   const unsigned row_span = (unsigned)max(row_hi - row_lo, 0);
 
-  TileCopy<D, BQ, NT> qcp, gcp;
+  // Q and dO tiles go straight from global memory to LDS; rows past n are
+  // clamped copies whose P (LSE = +inf) and dS (D = 0) are exactly zero.
+  using Tile = TileAsync<D, BQ, NT>;
   float st_val = 0.0f;  // staged row statistic (threads < 2*BQ)
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, int buf) {
     const int i0 = t * BQ;
-    qcp.load(Q + (size_t)i0 * D, n - i0, tid);
-    gcp.load(dO + (size_t)i0 * D, n - i0, tid);
+    Tile::issue(Q + (size_t)i0 * D, n - i0, tiles[buf][0], tid);
+    Tile::issue(dO + (size_t)i0 * D, n - i0, tiles[buf][1], tid);
     if (tid < 2 * BQ) {
       const int r = tid & (BQ - 1), i = i0 + r;
       if (tid < BQ)  // rows past the end get +inf so that P = 0 there
@@ -105,9 +105,7 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
         st_val = i < n ? dl[i] : 0.0f;
     }
   };
-  auto store_tile = [&](int buf) {
-    qcp.store(tiles[buf][0], tid);
-    gcp.store(tiles[buf][1], tid);
+  auto store_stats = [&](int buf) {
     if (tid < 2 * BQ) rowst[buf][tid / BQ][tid & (BQ - 1)] = st_val;
   };
 
@@ -119,15 +117,15 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   }
 
   if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
+    load_tile(t_lo, 0);
+    store_stats(0);
   }
-  __syncthreads();
+  wait_all_and_barrier();
 
   for (int t = t_lo; t < t_hi; ++t) {
     const int buf = (t - t_lo) & 1;
     const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
+    if (has_next) load_tile(t + 1, buf ^ 1);  // buffer released by the last barrier
     const __bf16* Qs = tiles[buf][0];
     const __bf16* dOs = tiles[buf][1];
     const int i0 = t * BQ;
@@ -175,8 +173,8 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
       }
     }
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    if (has_next) store_stats(buf ^ 1);
+    wait_all_and_barrier();
   }
 
   if (my_key < n) {
@@ -266,31 +264,26 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64) void bwd_q_bf16_kernel(
   if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
   const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
 
-  TileCopy<D, BC, NT> kcp, vcp;
-  auto load_tile = [&](int t) {
+  // K and V tiles go straight from global memory to LDS; key rows past n are
+  // clamped copies whose probabilities are masked to zero.
+  using Tile = TileAsync<D, BC, NT>;
+  auto load_tile = [&](int t, int buf) {
     const int kbase = t * BC;
-    kcp.load(K + (size_t)kbase * D, n - kbase, tid);
-    vcp.load(V + (size_t)kbase * D, n - kbase, tid);
-  };
-  auto store_tile = [&](int buf) {
-    kcp.store(tiles[buf][0], tid);
-    vcp.store(tiles[buf][1], tid);
+    Tile::issue(K + (size_t)kbase * D, n - kbase, tiles[buf][0], tid);
+    Tile::issue(V + (size_t)kbase * D, n - kbase, tiles[buf][1], tid);
   };
 
   f32x16 dq[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
+  if (t_lo < t_hi) load_tile(t_lo, 0);
+  wait_all_and_barrier();
 
   for (int t = t_lo; t < t_hi; ++t) {
     const int buf = (t - t_lo) & 1;
     const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
+    if (has_next) load_tile(t + 1, buf ^ 1);  // buffer released by the last barrier
     const __bf16* Ks = tiles[buf][0];
     const __bf16* Vs = tiles[buf][1];
     const int kbase = t * BC;
@@ -333,8 +326,7 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64) void bwd_q_bf16_kernel(
       for (int db = 0; db < NDB; ++db) dq[db] = mfma32(lds_col_frag<D>(Ks, 16 * st, 32 * db, lane), sb, dq[db]);
     }
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    wait_all_and_barrier();
   }
 
   if (my_row < n) {

@@ -52,6 +52,26 @@ __device__ __forceinline__ float swap_half(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over the lane pair (l, l^32), with v_permlane32_swap (a
+// VALU op; no LDS round trip).  The swap leaves lanes 0-31 of the first
+// result and 32-63 of the second holding their own value, the others the
+// partner's, so combining both results covers the pair on every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Instruction-scheduling hints (LLVM sched_group_barrier masks).
+enum : int { kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100,
+             kSchedDSWrite = 0x200 };
+#define EXATTN_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane L receives element L%4 of the 8-byte chunk addressed by lane 4k + L/4,
 // in its element k (k = 0..3).
@@ -108,6 +128,39 @@ struct TileCopy {
     }
   }
 };
+
+// Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout
+// (global_load_lds_dwordx4: lane i of a wave writes the 16 bytes at LDS
+// base + 16*i, so each lane fetches the logical chunk that belongs in its
+// slot; the XOR swizzle is its own inverse).  No registers are staged; the
+// data is in LDS once vmcnt drains.  Rows at or beyond `valid` (>= 1) re-read
+// row valid-1, so the caller must mask those rows out of every result.
+template <int D, int ROWS, int NT>
+struct TileAsync {
+  static constexpr int CPR = D / 8;
+  static constexpr int IT = ROWS * CPR / NT;
+  static_assert((ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
+  static __device__ __forceinline__ void issue(const __bf16* __restrict__ src, int valid, __bf16* lds, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int slot0 = it * NT + wave * 64;  // first chunk slot of this wave
+      const int p = slot0 + lane;
+      const int row = p / CPR;
+      const int c = swz_chunk<D>(row, p % CPR);
+      const int srow = row < valid ? row : valid - 1;
+      __builtin_amdgcn_global_load_lds(src + (size_t)srow * D + 8 * c,
+                                       (__attribute__((address_space(3))) void*)(lds + 8 * slot0), 16, 0, 0);
+    }
+  }
+};
+
+// Wait for every outstanding memory operation of this wave (including direct
+// global -> LDS copies), then synchronise the workgroup.
+__device__ __forceinline__ void wait_all_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
 
 // MFMA operand with k along d: lane reads 8 consecutive columns
 // [16*ds + 8*(lane/32), +8) of tile row `row`.

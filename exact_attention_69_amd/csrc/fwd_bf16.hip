@@ -14,11 +14,14 @@
 //   S^T (keys x rows) = K_tile * Q^T     32x32x16 bf16 MFMA; K from LDS,
 //                                        Q^T held in registers all along.
 //   each lane owns one query row (lane % 32) and 16 keys per 32-key block,
-//   so the row max/sum are in-lane reductions plus one swap with lane+32.
+//   so the row max/sum are in-lane reductions plus one lane-pair exchange.
 //   O^T (d x rows) += V_tile^T * P^T     P^T comes straight from the S^T
 //                                        accumulator registers (converted to
 //                                        bf16); V^T is read from LDS with the
 //                                        gfx950 transpose read.
+// Software pipeline: K tiles are staged one tile ahead of V tiles, so while
+// the vector ALU exponentiates tile t the matrix cores already compute S for
+// tile t+1; the two instruction streams are interleaved explicitly.
 // Scores are handled in the base-2 domain: exp(scale*s) = 2^(scale*log2e*s).
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -62,11 +65,9 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   constexpr int NDS = D / 16;   // 16-wide d steps
   constexpr int NDB = D / 32;   // 32-wide d blocks of the output
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BC * D];  // [buf][K/V]
+  __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vbuf[2][BC * D];
 
-  // XCD-aware block order: the hardware deals consecutive workgroups out to
-  // the 8 XCDs in turn; remap so that each XCD gets a contiguous range of
-  // (head, q-block) tiles and the q-blocks of one head share that XCD's L2.
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int head = bid / n_qblocks;
   const int qb = bid - head * n_qblocks;
@@ -91,19 +92,12 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     const bool ok = my_row < n;
     const u32x4* src = (const u32x4*)(Q + (size_t)(ok ? my_row : 0) * D + 8 * hi);
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      u32x4 v = ok ? src[2 * ds] : u32x4{0, 0, 0, 0};
-      qreg[ds] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int ds = 0; ds < NDS; ++ds) qreg[ds] = __builtin_bit_cast(bf16x8, ok ? src[2 * ds] : u32x4{0, 0, 0, 0});
   }
 
   // Key tiles this block visits (band of the whole block for a window).
   int k_lo = 0, k_hi = n;
-  if constexpr (WINDOWED) {
-    long a = (long)q0 - window, b = (long)q0 + BR - 1 + window + 1;
-    k_lo = a < 0 ? 0 : (int)a;
-    k_hi = b > n ? n : (int)b;
-  }
+  if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
   const int t_lo = k_lo / BC;
   const int t_hi = (k_hi + BC - 1) / BC;
   // keys visible to this lane's row
@@ -111,16 +105,16 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
   const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
 
-  // Global -> register staging of one K and one V tile (coalesced 16 B loads).
-  TileCopy<D, BC, NT> kcp, vcp;
-  auto load_tile = [&](int t) {
-    const int kbase = t * BC;
-    kcp.load(K + (size_t)kbase * D, n - kbase, tid);
-    vcp.load(V + (size_t)kbase * D, n - kbase, tid);
-  };
-  auto store_tile = [&](int buf) {
-    kcp.store(smem[buf][0], tid);
-    vcp.store(smem[buf][1], tid);
+  using Tile = TileAsync<D, BC, NT>;
+
+  // S^T for one K tile in LDS: lanes = query rows, registers = keys.
+  auto compute_s = [&](const __bf16* Ks, f32x16 (&s)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
   };
 
   f32x16 o[NDB];
@@ -129,41 +123,30 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   float m_run = kNegInf;  // running max, log2 domain (scale*log2e*s)
   float l_part = 0.0f;    // this lane's share of the running sum
 
+  // Prologue: K and V of the first tile, K of the second.  Key rows past n
+  // are clamped copies; their scores are masked to -inf (P = 0).
   if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
+    Tile::issue(K + (size_t)t_lo * BC * D, n - t_lo * BC, kbuf[0], tid);
+    Tile::issue(V + (size_t)t_lo * BC * D, n - t_lo * BC, vbuf[0], tid);
+    if (t_lo + 1 < t_hi) Tile::issue(K + (size_t)(t_lo + 1) * BC * D, n - (t_lo + 1) * BC, kbuf[1], tid);
   }
-  __syncthreads();
+  wait_all_and_barrier();
+  f32x16 s_cur[NKB];
+  compute_s(kbuf[0], s_cur);
 
   for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
-
-    const __bf16* Ks = smem[buf][0];
-    const __bf16* Vs = smem[buf][1];
+    const int j = t - t_lo;
+    // V of tile t+1 into the V buffer read last iteration, K of tile t+2 into
+    // the K buffer read last iteration (both released by the last barrier).
+    if (t + 1 < t_hi) Tile::issue(V + (size_t)(t + 1) * BC * D, n - (t + 1) * BC, vbuf[(j + 1) & 1], tid);
+    if (t + 2 < t_hi) Tile::issue(K + (size_t)(t + 2) * BC * D, n - (t + 2) * BC, kbuf[j & 1], tid);
     const int kbase = t * BC;
 
-    // ---- S^T = K Q^T ------------------------------------------------------
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        s[kb] = mfma32(lds_row_frag<D>(Ks, row, ds, hi), qreg[ds], s[kb]);
-      }
-    }
-
-    // ---- masks: key tail and sliding window --------------------------------
-    // Branch-free: one unsigned range test per element against this row's
-    // visible keys [key_lo, key_hi).
+    // ---- masks: key tail and sliding window (branch-free range test) -------
     bool need_mask = kbase + BC > n;
     if constexpr (WINDOWED) {
       const int r_lo = q0 + wave * 32, r_hi = r_lo + 31;
-      const int dist = max(r_hi - kbase, kbase + BC - 1 - r_lo);
-      need_mask = need_mask || dist > window;
+      need_mask = need_mask || max(r_hi - kbase, kbase + BC - 1 - r_lo) > window;
     }
     if (need_mask) {
 #pragma unroll
@@ -171,17 +154,17 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kbase + kb * 32 + acc_row(r, lane);
-          s[kb][r] = (unsigned)(key - key_lo) < key_span ? s[kb][r] : kNegInf;
+          s_cur[kb][r] = (unsigned)(key - key_lo) < key_span ? s_cur[kb][r] : kNegInf;
         }
     }
 
-    // ---- online softmax -----------------------------------------------------
+    // ---- running max and (rare) rescale -------------------------------------
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, swap_half(mx));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
+    mx = pair_max(mx);
     const float mx2 = mx * scale_log2;  // -inf stays -inf
     const bool grow = mx2 > m_run + kRescaleThreshold || (m_run == kNegInf && mx2 != kNegInf);
     if (__any(grow)) {
@@ -196,33 +179,64 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     }
     const float msub = m_run == kNegInf ? 0.0f : m_run;
 
+    // ---- S for the next tile (matrix cores) || exponentials (vector ALU) ----
+    // On the last tile this reads a stale K buffer; the result is unused.
+    f32x16 s_nxt[NKB];
+    compute_s(kbuf[(j + 1) & 1], s_nxt);
+    // P in bf16 (the operand of the P V product); the fp32 row sum is split
+    // over independent partial sums to keep the add chain short.
     bf16x8 pb[BC / 16];
+    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -msub));
-        l_part += s[kb][r];
+        s_cur[kb][r] = fast_exp2(__builtin_fmaf(s_cur[kb][r], scale_log2, -msub));
+        lsum[r & 3] += s_cur[kb][r];
       }
-      pb[2 * kb] = acc_to_operand(s[kb], 0);
-      pb[2 * kb + 1] = acc_to_operand(s[kb], 1);
+      pb[2 * kb] = acc_to_operand(s_cur[kb], 0);
+      pb[2 * kb + 1] = acc_to_operand(s_cur[kb], 1);
+    }
+    l_part += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    // Issue order: LDS reads run kLead MFMAs ahead so their latency hides
+    // behind earlier MFMAs; the exponentials fill the gaps.
+    {
+      constexpr int NS = NKB * NDS, kLead = 4;
+      constexpr int VPER = (4 * 16 * NKB + 8 * NKB) / NS + 1;
+      EXATTN_SCHED(kSchedDSRead, kLead);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        EXATTN_SCHED(kSchedMFMA, 1);
+        if (i + kLead < NS) EXATTN_SCHED(kSchedDSRead, 1);
+        EXATTN_SCHED(kSchedVALU, VPER);
+      }
     }
 
     // ---- O^T += V^T P^T -------------------------------------------------------
     // A operand (V^T): lane l needs V[key(t)][db*32 + l%32] with the keys in
     // the k order of pb (the transpose read delivers exactly that).
+    const __bf16* Vs = vbuf[j & 1];
 #pragma unroll
     for (int st = 0; st < BC / 16; ++st)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        o[db] = mfma32(lds_col_frag<D>(Vs, 16 * st, 32 * db, lane), pb[st], o[db]);
+      for (int db = 0; db < NDB; ++db) o[db] = mfma32(lds_col_frag<D>(Vs, 16 * st, 32 * db, lane), pb[st], o[db]);
+    {
+      constexpr int NP = (BC / 16) * NDB, kLead = 3;
+      EXATTN_SCHED(kSchedDSRead, 2 * kLead);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        EXATTN_SCHED(kSchedMFMA, 1);
+        if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
+      }
+    }
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    wait_all_and_barrier();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -----------------------
-  const float l_tot = l_part + swap_half(l_part);
+  const float l_tot = pair_sum(l_part);
   if (my_row < n) {
     const float inv = 1.0f / l_tot;
     __bf16* Orow = Og + head_off + (size_t)my_row * D;
