@@ -1,14 +1,19 @@
 """Benchmark: exact attention forward + backward on one MI355X.
 
-A step is one forward (attn_fwd) plus one backward (attn_bwd) over the whole
-batch of the n = 8192, d = 128 workload (B = 2, H = 32, bf16, Q scaled by 3),
-inputs resident in device memory.  Throughput counts the algorithmic FLOPs
+A step is one forward (attn_fwd) plus one backward (the three stage calls
+attn_bwd_rowdot, attn_bwd_dkdv, attn_bwd_dq -- exactly the kernels attn_bwd
+launches) over the whole batch of the n = 8192, d = 128 workload (B = 2,
+H = 32, bf16, Q scaled by 3), inputs resident in device memory.  Throughput counts the algorithmic FLOPs
 4*B*H*n^2*d (forward) + 10*B*H*n^2*d (backward), scaled by the fraction of
 (query, key) pairs a window lets through.
 
 Prints ONE JSON line.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--cpu-seconds S]
+                  [--no-cpu-baseline] [--cpu-seconds S] [--copy-calibration MIB]
+
+--copy-calibration MIB also runs one plain device-to-device copy of MIB MiB
+after the timed steps; under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give
+the counters' scale for a transfer of known size.
 """
 
 import argparse
@@ -75,11 +80,12 @@ def cpu_baseline(wl, seconds):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the attention path runs on a single device); "
@@ -106,43 +112,68 @@ def main(argv=None):
                      device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def fwd():
         ea.attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream)
-        ea.attn_bwd(q, k, v, o, do, lse, wl.scale, wl.window, workspace=ws, dq=dq, dk=dk, dv=dv, stream=stream)
 
+    # The backward runs as its three stage calls (the same three kernels that
+    # attn_bwd launches), so that every kernel is bracketed by its own events.
+    def bwd_stages():
+        return (lambda: ea.attn_bwd_rowdot(o, do, workspace=ws, stream=stream),
+                lambda: ea.attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=stream),
+                lambda: ea.attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=stream))
+
+    calls = (fwd,) + bwd_stages()
     for _ in range(args.warmup):
-        step()
+        for c in calls:
+            c()
     torch.cuda.synchronize()
 
-    # Whole steps, bracketed by device syncs, timed with events on the stream.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Whole steps, bracketed by device syncs, timed with events on the stream
+    # the kernels are launched on; one event between consecutive kernels.
+    nk = len(calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for s in range(args.steps):
         ev[s][0].record(stream)
-        ea.attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream)
-        ev[s][1].record(stream)
-        ea.attn_bwd(q, k, v, o, do, lse, wl.scale, wl.window, workspace=ws, dq=dq, dk=dk, dv=dv, stream=stream)
-        ev[s][2].record(stream)
+        for i, c in enumerate(calls):
+            c()
+            ev[s][i + 1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    kms = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / args.steps for i in range(nk)]
+    fwd_ms = kms[0]
+    bwd_ms = sum(kms[1:])
     ms = total_ms / args.steps
     peak = PEAK_TFLOPS[wl.dtype]
     value = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
 
-    # The forward is a single kernel launch per call, so its events time that
-    # kernel; its algorithmic FLOPs per launch are 4*B*H*pairs*d.
+    # Algorithmic FLOPs per launch of each kernel (pairs = visible (i, j)):
+    #   forward       4*B*H*pairs*d  (S = Q K^T and O = P V)
+    #   dK/dV pass    8*B*H*pairs*d  (S, dP = dO V^T, dV = P^T dO, dK = dS^T Q)
+    #   dQ pass       6*B*H*pairs*d  (S, dP, dQ = dS K)
+    #   rowdot        memory bound (reads O and dO, writes D)
+    kernel_flops = [fwd_f, None, 0.8 * bwd_f, 0.6 * bwd_f]
+    names = [f"fwd_bf16_kernel<{wl.d}>", f"bwd_rowdot_kernel<{wl.d}>", f"bwd_kv_bf16_kernel<{wl.d}>",
+             f"bwd_q_bf16_kernel<{wl.d}>"]
+    dom = max(range(nk), key=lambda i: kms[i])
+    ach = kernel_flops[dom] / (kms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "kernel": names[dom],
+                "algorithmic_flops_per_launch": kernel_flops[dom], "avg_launch_ms": round(kms[dom], 4)}
     fwd_tflops = fwd_f / (fwd_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(fwd_tflops / peak, 4), "traffic": None,
-                "kernel": f"fwd_bf16_kernel<{wl.d}> (attn_fwd, one launch per call)",
-                "algorithmic_flops_per_launch": fwd_f, "avg_launch_ms": round(fwd_ms, 4)}
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -152,6 +183,9 @@ def main(argv=None):
                    "q_mult": wl.q_mult, "scale": wl.scale},
         "pct_bf16_peak": round(100.0 * value / peak, 2),
         "detail": {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                   "kernel_ms": {names[i]: round(kms[i], 4) for i in range(nk)},
+                   "kernel_tflops": {names[i]: round(kernel_flops[i] / (kms[i] * 1e-3) / 1e12, 2)
+                                     for i in range(nk) if kernel_flops[i]},
                    "fwd_tflops": round(fwd_tflops, 2), "bwd_tflops": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 2),
                    "flops_per_step": fwd_f + bwd_f, "wall_s_timed": round(wall, 3),
                    "fwd_hbm_gbs_algorithmic": round(hbm_bytes(wl)[0] / (fwd_ms * 1e-3) / 1e9, 1),

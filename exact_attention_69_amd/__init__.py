@@ -10,6 +10,9 @@ from ._binding import (  # noqa: F401
     ExattnError,
     LIB_PATH,
     attn_bwd,
+    attn_bwd_dkdv,
+    attn_bwd_dq,
+    attn_bwd_rowdot,
     attn_bwd_workspace_bytes,
     attn_fwd,
     exattn_status_string,

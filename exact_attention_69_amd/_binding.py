@@ -45,6 +45,12 @@ def load_library(path=None):
     lib.attn_bwd_workspace_bytes.restype = cs
     lib.attn_bwd.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, vp, cs, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_bwd_rowdot.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, cs, vp]
+    lib.attn_bwd_rowdot.restype = ci
+    lib.attn_bwd_dkdv.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, cs, vp]
+    lib.attn_bwd_dkdv.restype = ci
+    lib.attn_bwd_dq.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, cs, vp]
+    lib.attn_bwd_dq.restype = ci
     lib.exattn_status_string.argtypes = [ci]
     lib.exattn_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -109,13 +115,19 @@ def attn_bwd_workspace_bytes(dtype_code, B, H, n, d):
     return int(load_library().attn_bwd_workspace_bytes(dtype_code, B, H, n, d))
 
 
+def _check_lse(lse, q):
+    torch = _torch()
+    B, H, n, _ = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, n]")
+
+
 def attn_bwd(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None, dk=None, dv=None, stream=None):
     """Backward pass.  Returns (dQ, dK, dV), each like q."""
     torch = _torch()
     _check_inputs(q, k, v, o, do)
+    _check_lse(lse, q)
     B, H, n, d = q.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, n]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     need = attn_bwd_workspace_bytes(code, B, H, n, d)
@@ -132,3 +144,64 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None
     if st != 0:
         raise ExattnError("attn_bwd", st, exattn_status_string(st))
     return dq, dk, dv
+
+
+def _workspace(q, code, workspace):
+    torch = _torch()
+    B, H, n, d = q.shape
+    need = attn_bwd_workspace_bytes(code, B, H, n, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def attn_bwd_rowdot(o, do, workspace=None, stream=None):
+    """Backward stage 1: D = rowsum(dO * O) into the workspace (returned)."""
+    torch = _torch()
+    _check_inputs(o, do)
+    B, H, n, d = o.shape
+    code = _dtype_code(o)
+    workspace, wsb = _workspace(o, code, workspace)
+    with torch.cuda.device(o.device):
+        st = load_library().attn_bwd_rowdot(code, B, H, n, d, o.data_ptr(), do.data_ptr(), workspace.data_ptr(),
+                                            wsb, _stream_ptr(o, stream))
+    if st != 0:
+        raise ExattnError("attn_bwd_rowdot", st, exattn_status_string(st))
+    return workspace
+
+
+def attn_bwd_dkdv(q, k, v, do, lse, workspace, scale=None, window=-1, dk=None, dv=None, stream=None):
+    """Backward stage 2: dK, dV (needs the workspace from attn_bwd_rowdot)."""
+    torch = _torch()
+    _check_inputs(q, k, v, do)
+    _check_lse(lse, q)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    with torch.cuda.device(q.device):
+        st = load_library().attn_bwd_dkdv(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          do.data_ptr(), lse.data_ptr(), scale, int(window), dk.data_ptr(),
+                                          dv.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), _stream_ptr(q, stream))
+    if st != 0:
+        raise ExattnError("attn_bwd_dkdv", st, exattn_status_string(st))
+    return dk, dv
+
+
+def attn_bwd_dq(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, stream=None):
+    """Backward stage 3: dQ (needs the workspace from attn_bwd_rowdot)."""
+    torch = _torch()
+    _check_inputs(q, k, v, do)
+    _check_lse(lse, q)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    with torch.cuda.device(q.device):
+        st = load_library().attn_bwd_dq(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(),
+                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        _stream_ptr(q, stream))
+    if st != 0:
+        raise ExattnError("attn_bwd_dq", st, exattn_status_string(st))
+    return dq

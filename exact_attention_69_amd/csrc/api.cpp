@@ -76,34 +76,108 @@ size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d) {
   return ((rows * sizeof(float) + 255) / 256) * 256;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// Validation shared by the backward entry points: every listed pointer is
+// non-null and 16-byte aligned, the workspace is large enough, no output
+// overlaps an input or another output.
+int check_bwd(int dtype, int B, int H, int n, int d, float scale, int window, const Span* ins, int nin,
+              const Span* outs, int nout, size_t workspace_bytes) {
+  int st = check_problem(dtype, B, H, n, d, scale, window);
+  if (st != EXATTN_OK) return st;
+  for (int i = 0; i < nin; ++i)
+    if (ins[i].p == nullptr || !aligned16(ins[i].p)) return EXATTN_EINVAL;
+  for (int i = 0; i < nout; ++i)
+    if (outs[i].p == nullptr || !aligned16(outs[i].p)) return EXATTN_EINVAL;
+  if (workspace_bytes < attn_bwd_workspace_bytes(dtype, B, H, n, d)) return EXATTN_EWORKSPACE;
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlaps(outs[o].p, outs[o].n, ins[i].p, ins[i].n)) return EXATTN_EINVAL;
+    for (int o2 = o + 1; o2 < nout; ++o2)
+      if (overlaps(outs[o].p, outs[o].n, outs[o2].p, outs[o2].n)) return EXATTN_EINVAL;
+  }
+  return EXATTN_OK;
+}
+
+int run_bwd(int dtype, const exattn::BwdParams& p, unsigned stages, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == EXATTN_BF16 ? exattn::launch_bwd_bf16(p, stages, s) : exattn::launch_bwd_f32(p, stages, s);
+  return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
 int attn_bwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
              const void* O, const void* dO, const float* LSE, float scale, int window, void* dQ,
              void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_problem(dtype, B, H, n, d, scale, window);
   if (st != EXATTN_OK) return st;
-  const void* ptrs[] = {Q, K, V, O, dO, LSE, dQ, dK, dV, workspace};
-  for (const void* p : ptrs)
-    if (p == nullptr || !aligned16(p)) return EXATTN_EINVAL;
-  size_t need = attn_bwd_workspace_bytes(dtype, B, H, n, d);
-  if (workspace_bytes < need) return EXATTN_EWORKSPACE;
-
-  size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
-  size_t lb = (size_t)B * H * n * sizeof(float);
-  struct Span { const void* p; size_t n; };
-  Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {O, tb}, {dO, tb}, {LSE, lb}};
-  Span outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {workspace, need}};
-  for (const Span& o : outs) {
-    for (const Span& i : ins)
-      if (overlaps(o.p, o.n, i.p, i.n)) return EXATTN_EINVAL;
-  }
-  for (int a = 0; a < 4; ++a)
-    for (int b = a + 1; b < 4; ++b)
-      if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return EXATTN_EINVAL;
-
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
+  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {O, tb}, {dO, tb}, {LSE, lb}};
+  const Span outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {workspace, wb}};
+  st = check_bwd(dtype, B, H, n, d, scale, window, ins, 6, outs, 4, workspace_bytes);
+  if (st != EXATTN_OK) return st;
   exattn::BwdParams p{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, B, H, n, d, scale, window};
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == EXATTN_BF16 ? exattn::launch_bwd_bf16(p, s) : exattn::launch_bwd_f32(p, s);
-  return from_hip(e);
+  return run_bwd(dtype, p, exattn::kStageAll, stream);
+}
+
+int attn_bwd_rowdot(int dtype, int B, int H, int n, int d, const void* O, const void* dO, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, 1.0f, -1);
+  if (st != EXATTN_OK) return st;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
+  const Span ins[] = {{O, tb}, {dO, tb}};
+  const Span outs[] = {{workspace, wb}};
+  st = check_bwd(dtype, B, H, n, d, 1.0f, -1, ins, 2, outs, 1, workspace_bytes);
+  if (st != EXATTN_OK) return st;
+  exattn::BwdParams p{nullptr, nullptr, nullptr, O, dO, nullptr, nullptr, nullptr, nullptr, (float*)workspace,
+                      B, H, n, d, 1.0f, -1};
+  return run_bwd(dtype, p, exattn::kStageRowdot, stream);
+}
+
+int attn_bwd_dkdv(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
+                  const void* dO, const float* LSE, float scale, int window, void* dK, void* dV,
+                  const void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, window);
+  if (st != EXATTN_OK) return st;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
+  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {LSE, lb}, {workspace, wb}};
+  const Span outs[] = {{dK, tb}, {dV, tb}};
+  st = check_bwd(dtype, B, H, n, d, scale, window, ins, 6, outs, 2, workspace_bytes);
+  if (st != EXATTN_OK) return st;
+  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, nullptr, dK, dV, (float*)workspace, B, H, n, d, scale, window};
+  return run_bwd(dtype, p, exattn::kStageKV, stream);
+}
+
+int attn_bwd_dq(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
+                const void* dO, const float* LSE, float scale, int window, void* dQ, const void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, window);
+  if (st != EXATTN_OK) return st;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
+  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {LSE, lb}, {workspace, wb}};
+  const Span outs[] = {{dQ, tb}};
+  st = check_bwd(dtype, B, H, n, d, scale, window, ins, 6, outs, 1, workspace_bytes);
+  if (st != EXATTN_OK) return st;
+  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, dQ, nullptr, nullptr, (float*)workspace, B, H, n, d, scale,
+                      window};
+  return run_bwd(dtype, p, exattn::kStageQ, stream);
 }
 
 }  // extern "C"

@@ -345,12 +345,9 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64) void bwd_q_bf16_kernel(
 }
 
 template <int D, bool W>
-hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
+hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const float scale_log2 = p.scale * kLog2e;
   const long heads = (long)p.B * p.H;
-  hipError_t e = launch_rowdot<__bf16>((const __bf16*)p.o, (const __bf16*)p.dout, p.delta, heads * p.n, D, stream);
-  if (e != hipSuccess) return e;
-
   constexpr int BKV = 32 * KvCfg<D>::NW;
   const int nkb = (p.n + BKV - 1) / BKV;
   const long tk = (long)nkb * heads;
@@ -359,25 +356,35 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   const long tq = (long)nqb * heads;
   if (tk > 0x7fffffffL || tq > 0x7fffffffL) return hipErrorInvalidValue;
 
-  hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(KvCfg<D>::NW * 64), 0, stream,
-                     (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
-                     p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(QCfg<D>::NW * 64), 0, stream,
-                     (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
-                     p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window);
-  return hipGetLastError();
+  if (stages & kStageRowdot) {
+    hipError_t e = launch_rowdot<__bf16>((const __bf16*)p.o, (const __bf16*)p.dout, p.delta, heads * p.n, D, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageKV) {
+    hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(KvCfg<D>::NW * 64), 0, stream,
+                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
+                       p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageQ) {
+    hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(QCfg<D>::NW * 64), 0, stream,
+                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
+                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const bool w = p.window >= 0;
   switch (p.d) {
-    case 64: return w ? bwd_d<64, true>(p, stream) : bwd_d<64, false>(p, stream);
-    case 128: return w ? bwd_d<128, true>(p, stream) : bwd_d<128, false>(p, stream);
-    case 256: return w ? bwd_d<256, true>(p, stream) : bwd_d<256, false>(p, stream);
+    case 64: return w ? bwd_d<64, true>(p, stages, stream) : bwd_d<64, false>(p, stages, stream);
+    case 128: return w ? bwd_d<128, true>(p, stages, stream) : bwd_d<128, false>(p, stages, stream);
+    case 256: return w ? bwd_d<256, true>(p, stages, stream) : bwd_d<256, false>(p, stages, stream);
     default: return hipErrorInvalidValue;
   }
 }

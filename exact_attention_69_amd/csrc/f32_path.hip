@@ -270,22 +270,30 @@ hipError_t fwd_d(const FwdParams& p, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
+hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const int nb = (p.n + ROWS - 1) / ROWS;
   const long total = (long)nb * p.B * p.H;
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
-  hipError_t e = launch_rowdot<float>((const float*)p.o, (const float*)p.dout, p.delta, (long)p.B * p.H * p.n, D,
-                                      stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
-                     (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dk,
-                     (float*)p.dv, p.n, nb, p.scale, p.window);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_q_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
-                     (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dq, p.n,
-                     nb, p.scale, p.window);
-  return hipGetLastError();
+  if (stages & kStageRowdot) {
+    hipError_t e = launch_rowdot<float>((const float*)p.o, (const float*)p.dout, p.delta, (long)p.B * p.H * p.n, D,
+                                        stream);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageKV) {
+    hipLaunchKernelGGL((bwd_kv_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
+                       (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dk,
+                       (float*)p.dv, p.n, nb, p.scale, p.window);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageQ) {
+    hipLaunchKernelGGL((bwd_q_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
+                       (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dq,
+                       p.n, nb, p.scale, p.window);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -299,11 +307,11 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
   }
 }
 
-hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_f32(const BwdParams& p, unsigned stages, hipStream_t stream) {
   switch (p.d) {
-    case 64: return bwd_d<64>(p, stream);
-    case 128: return bwd_d<128>(p, stream);
-    case 256: return bwd_d<256>(p, stream);
+    case 64: return bwd_d<64>(p, stages, stream);
+    case 128: return bwd_d<128>(p, stages, stream);
+    case 256: return bwd_d<256>(p, stages, stream);
     default: return hipErrorInvalidValue;
   }
 }

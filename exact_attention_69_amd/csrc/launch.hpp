@@ -35,8 +35,10 @@ struct BwdParams {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
+// Backward stages: rowdot (D), key side (dK, dV), query side (dQ).
+enum BwdStage : unsigned { kStageRowdot = 1, kStageKV = 2, kStageQ = 4, kStageAll = 7 };
+hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdParams& p, unsigned stages, hipStream_t stream);
 
 // Band of the sliding window, used to skip tiles (host and device).
 // Keys [lo, hi) that any row in [r0, r1) may attend to.

@@ -123,6 +123,42 @@ int attn_bwd(int dtype, int B, int H, int n, int d,
              void *workspace, size_t workspace_bytes,
              void *stream);
 
+/*
+ * The backward as three stages, each exactly one kernel launch; attn_bwd is
+ * these three in order on one stream.  Stage 1 must complete before stages
+ * 2 and 3 (stream order does it); stages 2 and 3 are independent of each
+ * other (they may run on two streams once stage 1 is done) and either may
+ * be skipped when its gradients are not wanted.  Arguments mean what they
+ * mean for attn_bwd; `workspace` carries D from stage 1 to stages 2 and 3
+ * and must not be modified in between.
+ *
+ * attn_bwd_rowdot: D_i = sum_k dO_ik * O_ik (fp32, into the workspace).
+ */
+int attn_bwd_rowdot(int dtype, int B, int H, int n, int d,
+                    const void *O, const void *dO,
+                    void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* attn_bwd_dkdv: dK and dV (key-side pass: each workgroup owns a block of
+ * keys and sweeps the query tiles of its band). */
+int attn_bwd_dkdv(int dtype, int B, int H, int n, int d,
+                  const void *Q, const void *K, const void *V,
+                  const void *dO, const float *LSE,
+                  float scale, int window,
+                  void *dK, void *dV,
+                  const void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* attn_bwd_dq: dQ (query-side pass: each workgroup owns a block of query
+ * rows and sweeps the key tiles of its band, recomputing P and dP). */
+int attn_bwd_dq(int dtype, int B, int H, int n, int d,
+                const void *Q, const void *K, const void *V,
+                const void *dO, const float *LSE,
+                float scale, int window,
+                void *dQ,
+                const void *workspace, size_t workspace_bytes,
+                void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *exattn_status_string(int status);
 

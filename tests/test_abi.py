@@ -36,7 +36,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "exattn_status_string"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rowdot",
+                                    "attn_bwd_workspace_bytes", "attn_fwd", "exattn_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -123,6 +124,22 @@ def test_backward_rejects_bad_arguments(lib):
     alias = list(p)
     alias[8] = p[7]  # dV aliases dK
     assert bwd(lib, p=alias, ws_bytes=need) == EINVAL
+
+
+def test_backward_stages_reject_bad_arguments(lib):
+    need = lib.attn_bwd_workspace_bytes(1, 1, 1, 128, 64)
+    q, k, v, do, lse, dk, dv, ws = ptrs(8)
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, ws, need - 1, None) == EWORKSPACE
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, None, ws, need, None) == EINVAL
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, q, need, None) == EINVAL  # workspace aliases O
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 72, q, do, ws, need, None) == EUNSUPPORTED
+    assert lib.attn_bwd_dkdv(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, dk, dv, ws, need - 1, None) == EWORKSPACE
+    assert lib.attn_bwd_dkdv(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, dk, dk, ws, need, None) == EINVAL
+    assert lib.attn_bwd_dkdv(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -3, dk, dv, ws, need, None) == EINVAL
+    assert lib.attn_bwd_dkdv(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, dk, ws, ws, need, None) == EINVAL
+    assert lib.attn_bwd_dq(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, dk, ws, need - 1, None) == EWORKSPACE
+    assert lib.attn_bwd_dq(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, k, ws, need, None) == EINVAL
+    assert lib.attn_bwd_dq(1, 1, 1, 128, 64, q, k, v, do, None, 0.1, -1, dk, ws, need, None) == EINVAL
 
 
 def test_binding_rejects_host_tensors():
