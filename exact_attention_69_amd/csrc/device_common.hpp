@@ -129,6 +129,21 @@ struct TileCopy {
   }
 };
 
+// One direct global -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes
+// at `gsrc` land at LDS address `lds_wave_base` + 16*i (base wave-uniform).
+// Issued through inline asm so that the compiler does not treat the copy as
+// an LDS store it must wait for before every later LDS read (it cannot tell
+// that the reads address other buffers); the callers wait explicitly
+// (wait_all_and_barrier) before any wave reads the filled buffer.  Nothing
+// else in the loops that use it touches vector memory.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds_wave_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 // Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout
 // (global_load_lds_dwordx4: lane i of a wave writes the 16 bytes at LDS
 // base + 16*i, so each lane fetches the logical chunk that belongs in its
@@ -149,8 +164,7 @@ struct TileAsync {
       const int row = p / CPR;
       const int c = swz_chunk<D>(row, p % CPR);
       const int srow = row < valid ? row : valid - 1;
-      __builtin_amdgcn_global_load_lds(src + (size_t)srow * D + 8 * c,
-                                       (__attribute__((address_space(3))) void*)(lds + 8 * slot0), 16, 0, 0);
+      lds_dma16(src + (size_t)srow * D + 8 * c, lds + 8 * slot0);
     }
   }
 };
