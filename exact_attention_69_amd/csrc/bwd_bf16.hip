@@ -51,7 +51,7 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
 
   __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BQ * D];  // [buf][Q/dO]
   __shared__ __attribute__((aligned(16))) __bf16 vres[BKV * D];        // this block's V rows
-  __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE*log2e / D]
+  __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE / D]
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int head = bid / n_kblocks;
@@ -84,29 +84,24 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   int q_lo = 0, q_hi = n;
   if constexpr (WINDOWED) band_keys(kb0, kb0 + BKV, n, window, &q_lo, &q_hi);
   const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
-  // query rows that see this lane's key (the window is symmetric)
+  // query rows that see this lane's key (the window is symmetric), within n
   int row_lo = 0, row_hi = n;
   if constexpr (WINDOWED) band_keys(my_key, my_key + 1, n, window, &row_lo, &row_hi);
   const unsigned row_span = (unsigned)max(row_hi - row_lo, 0);
 
-  // Q and dO tiles go straight from global memory to LDS; rows past n are
-  // clamped copies whose P (LSE = +inf) and dS (D = 0) are exactly zero.
+  // Q and dO tiles, and the LSE and D values of their rows, go straight from
+  // global memory to LDS.  Rows past n are clamped copies of row n-1; their
+  // probabilities are masked to zero on the tail tile.
   using Tile = TileAsync<D, BQ, NT>;
-  float st_val = 0.0f;  // staged row statistic (threads < 2*BQ)
+  static_assert(BQ == 32, "the row-statistics copy maps 64 lanes to 2 x 32 rows");
   auto load_tile = [&](int t, int buf) {
     const int i0 = t * BQ;
     Tile::issue(Q + (size_t)i0 * D, n - i0, tiles[buf][0], tid);
     Tile::issue(dO + (size_t)i0 * D, n - i0, tiles[buf][1], tid);
-    if (tid < 2 * BQ) {
-      const int r = tid & (BQ - 1), i = i0 + r;
-      if (tid < BQ)  // rows past the end get +inf so that P = 0 there
-        st_val = i < n ? lse[i] * kLog2e : __builtin_huge_valf();
-      else
-        st_val = i < n ? dl[i] : 0.0f;
+    if (wave == 0) {  // lanes 0-31: LSE of rows i0.., lanes 32-63: D
+      const int i = min(i0 + l32, n - 1);
+      lds_dma4(hi ? (const void*)(dl + i) : (const void*)(lse + i), &rowst[buf][0][0]);
     }
-  };
-  auto store_stats = [&](int buf) {
-    if (tid < 2 * BQ) rowst[buf][tid / BQ][tid & (BQ - 1)] = st_val;
   };
 
   f32x16 dk[NDB], dv[NDB];
@@ -116,10 +111,7 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
     dv[i] = f32x16{};
   }
 
-  if (t_lo < t_hi) {
-    load_tile(t_lo, 0);
-    store_stats(0);
-  }
+  if (t_lo < t_hi) load_tile(t_lo, 0);
   wait_all_and_barrier();
 
   for (int t = t_lo; t < t_hi; ++t) {
@@ -138,10 +130,12 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
       dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), lds_row_frag<D>(vres, wave * 32 + l32, ds, hi), dp);
     }
 
-    bool need_mask = false;
+    // Rows past n (tail tile) and, with a window, queries outside this
+    // lane's key band get P = 0.
+    bool need_mask = i0 + BQ > n;
     if constexpr (WINDOWED) {
       const int k_lo_w = kb0 + wave * 32;
-      need_mask = max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
+      need_mask = need_mask || max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -151,11 +145,9 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g + j;
-        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j]));
-        if constexpr (WINDOWED) {
-          // queries that see this lane's key: [row_lo, row_lo + row_span)
-          if (need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
-        }
+        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j] * kLog2e));
+        // queries that see this lane's key: [row_lo, row_lo + row_span)
+        if (need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
         s[r] = p;
         dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
       }
@@ -173,7 +165,6 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
       }
     }
 
-    if (has_next) store_stats(buf ^ 1);
     wait_all_and_barrier();
   }
 

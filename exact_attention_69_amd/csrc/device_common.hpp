@@ -144,6 +144,16 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds_wave
                : "memory", "m0");
 }
 
+// 4-byte variant (global_load_lds_dword): lane i's 4 bytes land at
+// `lds_wave_base` + 4*i.
+__device__ __forceinline__ void lds_dma4(const void* gsrc, const void* lds_wave_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 // Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout
 // (global_load_lds_dwordx4: lane i of a wave writes the 16 bytes at LDS
 // base + 16*i, so each lane fetches the logical chunk that belongs in its

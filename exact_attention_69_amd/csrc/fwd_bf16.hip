@@ -1,24 +1,28 @@
 // Forward attention kernel, bf16 inputs, fp32 accumulation, gfx950.
 //
-// Tiled forward with an online softmax: each workgroup owns BR = 32*NW query
-// rows of one (batch, head) and streams key/value tiles of BC rows through
-// LDS, keeping per row a running maximum m and a running sum l and rescaling
-// the output accumulator when m grows, so the result equals the one-shot
-// softmax (llmis.ru chapter 3.1 "The cost of attention", section 5; the
-// unite.ai page "Flash Attention: Revolucionando a Eficiencia dos Modelos
-// Transformer", sections "O Algoritmo de Flash Attention" and "A Matematica
-// por tras da Flash Attention").  Only O and the per-row log-sum-exp are
-// written; the score tile lives in registers.
+// Tiled forward with an online softmax: each workgroup owns BR query rows of
+// one (batch, head) and streams key/value tiles of BC rows through LDS,
+// keeping per row a running maximum m and a running sum l and rescaling the
+// output accumulator when m grows, so the result equals the one-shot softmax
+// (llmis.ru chapter 3.1 "The cost of attention", section 5; the unite.ai page
+// "Flash Attention: Revolucionando a Eficiencia dos Modelos Transformer",
+// sections "O Algoritmo de Flash Attention" and "A Matematica por tras da
+// Flash Attention").  Only O and the per-row log-sum-exp are written; the
+// score tile lives in registers.
 //
-// Data flow per wave (32 query rows):
+// Data flow per wave (RB blocks of 32 query rows):
 //   S^T (keys x rows) = K_tile * Q^T     32x32x16 bf16 MFMA; K from LDS,
 //                                        Q^T held in registers all along.
-//   each lane owns one query row (lane % 32) and 16 keys per 32-key block,
-//   so the row max/sum are in-lane reductions plus one lane-pair exchange.
+//   each lane owns one query row per row block (lane % 32) and 16 keys per
+//   32-key block, so the row max/sum are in-lane reductions plus one
+//   lane-pair exchange.
 //   O^T (d x rows) += V_tile^T * P^T     P^T comes straight from the S^T
 //                                        accumulator registers (converted to
 //                                        bf16); V^T is read from LDS with the
 //                                        gfx950 transpose read.
+// Every K and V^T fragment read from LDS feeds RB matrix products (one per
+// row block), so RB = 2 halves the LDS traffic per FLOP at the price of a
+// 512-register, one-wave-per-SIMD budget.
 // Software pipeline: K tiles are staged one tile ahead of V tiles, so while
 // the vector ALU exponentiates tile t the matrix cores already compute S for
 // tile t+1; the two instruction streams are interleaved explicitly.
@@ -35,21 +39,21 @@ namespace {
 // normalisation uses the same max, so the result is unchanged.
 constexpr float kRescaleThreshold = 8.0f;
 
-// NW waves per workgroup (32 query rows each), BC keys per tile, WPE the
-// waves per SIMD the register budget is sized for.
+// NW waves per workgroup, RB blocks of 32 query rows per wave, BC keys per
+// tile, WPE the waves per SIMD the register budget is sized for.
 template <int D>
 struct FwdCfg;
 template <>
 struct FwdCfg<64> {
-  static constexpr int NW = 4, BC = 64, WPE = 2;
+  static constexpr int NW = 4, RB = 1, BC = 64, WPE = 2;
 };
 template <>
 struct FwdCfg<128> {
-  static constexpr int NW = 4, BC = 64, WPE = 2;
+  static constexpr int NW = 4, RB = 1, BC = 64, WPE = 2;
 };
 template <>
 struct FwdCfg<256> {
-  static constexpr int NW = 4, BC = 32, WPE = 1;
+  static constexpr int NW = 4, RB = 1, BC = 32, WPE = 1;
 };
 
 template <int D, bool WINDOWED>
@@ -58,8 +62,9 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n_qblocks, int total_blocks,
     float scale_log2, int window) {
   constexpr int NW = FwdCfg<D>::NW;
+  constexpr int RB = FwdCfg<D>::RB;
   constexpr int BC = FwdCfg<D>::BC;
-  constexpr int BR = 32 * NW;
+  constexpr int BR = 32 * RB * NW;
   constexpr int NT = NW * 64;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NDS = D / 16;   // 16-wide d steps
@@ -84,15 +89,20 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   const __bf16* V = Vg + head_off;
 
   const int q0 = qb * BR;
-  const int my_row = q0 + wave * 32 + l32;
-
-  // Q^T operand, kept in registers: lane holds Q[my_row][16*ds + 8*hi .. +8].
-  bf16x8 qreg[NDS];
-  {
-    const bool ok = my_row < n;
-    const u32x4* src = (const u32x4*)(Q + (size_t)(ok ? my_row : 0) * D + 8 * hi);
+  const int w0 = q0 + wave * 32 * RB;  // first row of this wave
+  int my_row[RB];
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qreg[ds] = __builtin_bit_cast(bf16x8, ok ? src[2 * ds] : u32x4{0, 0, 0, 0});
+  for (int rb = 0; rb < RB; ++rb) my_row[rb] = w0 + 32 * rb + l32;
+
+  // Q^T operands, kept in registers: lane holds Q[my_row][16*ds + 8*hi .. +8].
+  bf16x8 qreg[RB][NDS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const bool ok = my_row[rb] < n;
+    const u32x4* src = (const u32x4*)(Q + (size_t)(ok ? my_row[rb] : 0) * D + 8 * hi);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+      qreg[rb][ds] = __builtin_bit_cast(bf16x8, ok ? src[2 * ds] : u32x4{0, 0, 0, 0});
   }
 
   // Key tiles this block visits (band of the whole block for a window).
@@ -100,28 +110,47 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
   const int t_lo = k_lo / BC;
   const int t_hi = (k_hi + BC - 1) / BC;
-  // keys visible to this lane's row
-  int key_lo = 0, key_hi = n;
-  if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
-  const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
+  // keys visible to each of this lane's rows
+  int key_lo[RB];
+  unsigned key_span[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    int lo = 0, hi_k = n;
+    if constexpr (WINDOWED) band_keys(my_row[rb], my_row[rb] + 1, n, window, &lo, &hi_k);
+    key_lo[rb] = lo;
+    key_span[rb] = (unsigned)max(hi_k - lo, 0);
+  }
 
   using Tile = TileAsync<D, BC, NT>;
 
-  // S^T for one K tile in LDS: lanes = query rows, registers = keys.
-  auto compute_s = [&](const __bf16* Ks, f32x16 (&s)[NKB]) {
+  // S^T for one K tile in LDS: lanes = query rows, registers = keys.  Each K
+  // fragment feeds the RB row blocks.
+  auto compute_s = [&](const __bf16* Ks, f32x16 (&s)[RB][NKB]) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[rb][kb] = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 a = lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma32(a, qreg[rb][ds], s[rb][kb]);
+      }
   };
 
-  f32x16 o[NDB];
+  f32x16 o[RB][NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
-  float m_run = kNegInf;  // running max, log2 domain (scale*log2e*s)
-  float l_part = 0.0f;    // this lane's share of the running sum
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[rb][i] = f32x16{};
+  float m_run[RB], l_part[RB];  // running max (log2 domain) and this lane's share of the sum
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = kNegInf;
+    l_part[rb] = 0.0f;
+  }
 
   // Prologue: K and V of the first tile, K of the second.  Key rows past n
   // are clamped copies; their scores are masked to -inf (P = 0).
@@ -131,7 +160,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     if (t_lo + 1 < t_hi) Tile::issue(K + (size_t)(t_lo + 1) * BC * D, n - (t_lo + 1) * BC, kbuf[1], tid);
   }
   wait_all_and_barrier();
-  f32x16 s_cur[NKB];
+  f32x16 s_cur[RB][NKB];
   compute_s(kbuf[0], s_cur);
 
   for (int t = t_lo; t < t_hi; ++t) {
@@ -145,68 +174,77 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     // ---- masks: key tail and sliding window (branch-free range test) -------
     bool need_mask = kbase + BC > n;
     if constexpr (WINDOWED) {
-      const int r_lo = q0 + wave * 32, r_hi = r_lo + 31;
-      need_mask = need_mask || max(r_hi - kbase, kbase + BC - 1 - r_lo) > window;
+      const int r_hi = w0 + 32 * RB - 1;
+      need_mask = need_mask || max(r_hi - kbase, kbase + BC - 1 - w0) > window;
     }
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + kb * 32 + acc_row(r, lane);
-          s_cur[kb][r] = (unsigned)(key - key_lo) < key_span ? s_cur[kb][r] : kNegInf;
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + kb * 32 + acc_row(r, lane);
+            s_cur[rb][kb][r] = (unsigned)(key - key_lo[rb]) < key_span[rb] ? s_cur[rb][kb][r] : kNegInf;
+          }
     }
 
     // ---- running max and (rare) rescale -------------------------------------
-    float mx = kNegInf;
+    float msub[RB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
-    mx = pair_max(mx);
-    const float mx2 = mx * scale_log2;  // -inf stays -inf
-    const bool grow = mx2 > m_run + kRescaleThreshold || (m_run == kNegInf && mx2 != kNegInf);
-    if (__any(grow)) {
-      const float m_new = grow ? mx2 : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // m_run=-inf -> 0
-      l_part *= alpha;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[rb][kb][r]);
+      mx = pair_max(mx);
+      const float mx2 = mx * scale_log2;  // -inf stays -inf
+      const bool grow = mx2 > m_run[rb] + kRescaleThreshold || (m_run[rb] == kNegInf && mx2 != kNegInf);
+      if (__any(grow)) {
+        const float m_new = grow ? mx2 : m_run[rb];
+        const float alpha = grow ? fast_exp2(m_run[rb] - m_new) : 1.0f;  // m_run=-inf -> 0
+        l_part[rb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
+        m_run[rb] = m_new;
+      }
+      msub[rb] = m_run[rb] == kNegInf ? 0.0f : m_run[rb];
     }
-    const float msub = m_run == kNegInf ? 0.0f : m_run;
 
     // ---- S for the next tile (matrix cores) || exponentials (vector ALU) ----
     // On the last tile this reads a stale K buffer; the result is unused.
-    f32x16 s_nxt[NKB];
+    f32x16 s_nxt[RB][NKB];
     compute_s(kbuf[(j + 1) & 1], s_nxt);
     // P in bf16 (the operand of the P V product); the fp32 row sum is split
     // over independent partial sums to keep the add chain short.
-    bf16x8 pb[BC / 16];
-    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 pb[RB][BC / 16];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s_cur[kb][r] = fast_exp2(__builtin_fmaf(s_cur[kb][r], scale_log2, -msub));
-        lsum[r & 3] += s_cur[kb][r];
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s_cur[rb][kb][r] = fast_exp2(__builtin_fmaf(s_cur[rb][kb][r], scale_log2, -msub[rb]));
+          lsum[r & 3] += s_cur[rb][kb][r];
+        }
+        pb[rb][2 * kb] = acc_to_operand(s_cur[rb][kb], 0);
+        pb[rb][2 * kb + 1] = acc_to_operand(s_cur[rb][kb], 1);
       }
-      pb[2 * kb] = acc_to_operand(s_cur[kb], 0);
-      pb[2 * kb + 1] = acc_to_operand(s_cur[kb], 1);
+      l_part[rb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     }
-    l_part += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-    // Issue order: LDS reads run kLead MFMAs ahead so their latency hides
+    // Issue order: LDS reads run kLead reads ahead so their latency hides
     // behind earlier MFMAs; the exponentials fill the gaps.
     {
       constexpr int NS = NKB * NDS, kLead = 4;
-      constexpr int VPER = (4 * 16 * NKB + 8 * NKB) / NS + 1;
+      constexpr int VPER = RB * (4 * 16 * NKB + 8 * NKB) / NS + 1;
       EXATTN_SCHED(kSchedDSRead, kLead);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        EXATTN_SCHED(kSchedMFMA, 1);
+        EXATTN_SCHED(kSchedMFMA, RB);
         if (i + kLead < NS) EXATTN_SCHED(kSchedDSRead, 1);
         EXATTN_SCHED(kSchedVALU, VPER);
       }
@@ -219,44 +257,53 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
 #pragma unroll
     for (int st = 0; st < BC / 16; ++st)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] = mfma32(lds_col_frag<D>(Vs, 16 * st, 32 * db, lane), pb[st], o[db]);
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 a = lds_col_frag<D>(Vs, 16 * st, 32 * db, lane);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(a, pb[rb][st], o[rb][db]);
+      }
     {
       constexpr int NP = (BC / 16) * NDB, kLead = 3;
       EXATTN_SCHED(kSchedDSRead, 2 * kLead);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        EXATTN_SCHED(kSchedMFMA, 1);
+        EXATTN_SCHED(kSchedMFMA, RB);
         if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
       }
     }
 
     wait_all_and_barrier();
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s_cur[rb][kb] = s_nxt[rb][kb];
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -----------------------
-  const float l_tot = pair_sum(l_part);
-  if (my_row < n) {
-    const float inv = 1.0f / l_tot;
-    __bf16* Orow = Og + head_off + (size_t)my_row * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = pair_sum(l_part[rb]);
+    if (my_row[rb] < n) {
+      const float inv = 1.0f / l_tot;
+      __bf16* Orow = Og + head_off + (size_t)my_row[rb] * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = db * 32 + 8 * g + 4 * hi;
-        u32x2 w;
-        w[0] = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2*)(Orow + dd) = w;
-      }
-    if (hi == 0) LSEg[(size_t)head * n + my_row] = kLn2 * (m_run + fast_log2(l_tot));
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dd = db * 32 + 8 * g + 4 * hi;
+          u32x2 w;
+          w[0] = pack_bf16x2(o[rb][db][4 * g + 0] * inv, o[rb][db][4 * g + 1] * inv);
+          w[1] = pack_bf16x2(o[rb][db][4 * g + 2] * inv, o[rb][db][4 * g + 3] * inv);
+          *(u32x2*)(Orow + dd) = w;
+        }
+      if (hi == 0) LSEg[(size_t)head * n + my_row[rb]] = kLn2 * (m_run[rb] + fast_log2(l_tot));
+    }
   }
 }
 
 template <int D, bool W>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  constexpr int BR = 32 * FwdCfg<D>::NW;
+  constexpr int BR = 32 * FwdCfg<D>::RB * FwdCfg<D>::NW;
   const int nqb = (p.n + BR - 1) / BR;
   const long total = (long)nqb * p.B * p.H;
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
