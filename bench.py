@@ -47,6 +47,31 @@ def hbm_bytes(wl):
     return 4 * t + r, 8 * t + 3 * r
 
 
+def measured_traffic(wl, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
+    (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size), or None
+    when the summary is for another workload or the kernel sources changed
+    since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters_n8192_d128.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    info = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "exact_attention_69_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    if info.get("workload") != wl.name or info.get("source_sha256") != h.hexdigest():
+        return None
+    k = info["kernels"].get(kernel)
+    return None if k is None else int(k["hbm_bytes_per_launch"])
+
+
 def cpu_baseline(wl, seconds):
     """Time the fp64 oracle (as it stands) on whole heads of the workload
     until about `seconds` of CPU work; report TFLOP/s on the same FLOP count."""
@@ -163,7 +188,7 @@ def main(argv=None):
     dom = max(range(nk), key=lambda i: kms[i])
     ach = kernel_flops[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None, "kernel": names[dom],
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(wl, names[dom]), "kernel": names[dom],
                 "algorithmic_flops_per_launch": kernel_flops[dom], "avg_launch_ms": round(kms[dom], 4)}
     fwd_tflops = fwd_f / (fwd_ms * 1e-3) / 1e12
 
