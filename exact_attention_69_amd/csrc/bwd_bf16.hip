@@ -30,7 +30,7 @@ namespace {
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvCfg {
-  static constexpr int NW = 4;   // waves; each owns 32 keys
+  static constexpr int NW = D == 128 ? 8 : 4;  // waves; each owns 32 keys
   static constexpr int BQ = 32;  // query rows per tile
   static constexpr int WPE = D == 256 ? 1 : 2;  // waves per SIMD
 };
@@ -194,19 +194,19 @@ template <int D>
 struct QCfg;
 template <>
 struct QCfg<64> {
-  static constexpr int NW = 4, BC = 64;
+  static constexpr int NW = 4, BC = 64, WPE = 2;
 };
 template <>
 struct QCfg<128> {
-  static constexpr int NW = 4, BC = 32;
+  static constexpr int NW = 8, BC = 32, WPE = 2;
 };
 template <>
 struct QCfg<256> {
-  static constexpr int NW = 4, BC = 32;
+  static constexpr int NW = 4, BC = 32, WPE = 1;
 };
 
 template <int D, bool WINDOWED>
-__global__ __launch_bounds__(QCfg<D>::NW * 64) void bwd_q_bf16_kernel(
+__global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
     __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window) {
