@@ -13,6 +13,8 @@ routine); nothing in this package is "parity unpinned".
 from .attention import (  # noqa: F401
     attention_forward,
     attention_backward,
+    attention_forward_gqa,
+    attention_backward_gqa,
     attention_probs,
     key_range,
     keys_per_row,

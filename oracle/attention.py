@@ -47,6 +47,8 @@ it equals the fully masked dense form).
 import numpy as np
 
 __all__ = [
+    "attention_forward_gqa",
+    "attention_backward_gqa",
     "key_range",
     "keys_per_row",
     "attention_probs",
@@ -246,3 +248,36 @@ def merge_partial_outputs(O_x, lse_x, O_y, lse_y):
     wx = np.exp(lse_x - lse)[..., None]
     wy = np.exp(lse_y - lse)[..., None]
     return wx * O_x + wy * O_y, lse
+
+
+def _group_size(q, k):
+    H, Hkv = q.shape[-3], k.shape[-3]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"query heads ({H}) must be a multiple of key/value heads ({Hkv})")
+    return H // Hkv
+
+
+def attention_forward_gqa(q, k, v, scale, window=-1, **kw):
+    """Grouped-query attention forward (the FlashAttention-2 variants of the
+    unite.ai page, section "FlashAttention-2", item 3).
+
+    ``q``: (B, H, n, d); ``k``, ``v``: (B, Hkv, n, d) with H a multiple of
+    Hkv.  Query head h attends with key/value head h // (H / Hkv): the query
+    heads of one group are consecutive (Hkv = 1 is multi-query attention,
+    Hkv = H the plain multi-head case).  Defined as ordinary attention with
+    each key/value head repeated for its group.
+    """
+    G = _group_size(q, k)
+    return attention_forward(q, np.repeat(np.asarray(k), G, axis=-3), np.repeat(np.asarray(v), G, axis=-3),
+                             scale, window, **kw)
+
+
+def attention_backward_gqa(q, k, v, do, scale, window=-1, **kw):
+    """Gradients of grouped-query attention: dQ per query head; dK and dV of a
+    key/value head are the sums over the query heads of its group (each
+    repeated copy of K and V receives its own gradient)."""
+    G = _group_size(q, k)
+    dq, dk, dv = attention_backward(q, np.repeat(np.asarray(k), G, axis=-3), np.repeat(np.asarray(v), G, axis=-3),
+                                    do, scale, window, **kw)
+    shp = k.shape[:-3] + (k.shape[-3], G) + k.shape[-2:]
+    return dq, dk.reshape(shp).sum(axis=-3), dv.reshape(shp).sum(axis=-3)

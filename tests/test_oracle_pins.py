@@ -202,6 +202,58 @@ def test_matches_torch_sdpa_and_autograd(n, d, window):
 
 
 # --------------------------------------------------------------------------
+# Grouped-query attention (K/V heads shared by groups of query heads)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (4, 2), (6, 1), (8, 2)])
+@pytest.mark.parametrize("window", [-1, 2])
+def test_gqa_matches_torch_sdpa_enable_gqa(H, Hkv, window):
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    n, d = 11, 6
+    s = 1.0 / math.sqrt(d)
+    q, do = rand(2, H, n, d), rand(2, H, n, d)
+    k, v = rand(2, Hkv, n, d), rand(2, Hkv, n, d)
+    O, lse = oracle.attention_forward_gqa(q, k, v, s, window)
+    dq, dk, dv = oracle.attention_backward_gqa(q, k, v, do, s, window)
+    assert dk.shape == k.shape and dv.shape == v.shape and dq.shape == q.shape
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    mask = torch.tensor(window_mask(n, window))
+    tO = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=s, enable_gqa=True)
+    tO.backward(torch.tensor(do, dtype=torch.float64))
+    np.testing.assert_allclose(O, tO.detach().numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_gqa_with_one_group_is_multi_head():
+    q, k, v, do = rand(1, 3, 9, 4), rand(1, 3, 9, 4), rand(1, 3, 9, 4), rand(1, 3, 9, 4)
+    a = oracle.attention_forward_gqa(q, k, v, 0.5) + oracle.attention_backward_gqa(q, k, v, do, 0.5)
+    b = oracle.attention_forward(q, k, v, 0.5) + oracle.attention_backward(q, k, v, do, 0.5)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_gqa_identical_query_heads_scale_kv_gradients():
+    # If every query head of a group carries the same Q and dO, the group's
+    # dK and dV are G times those of a single head.
+    n, d, G = 10, 4, 3
+    q1, do1 = rand(1, 1, n, d), rand(1, 1, n, d)
+    k, v = rand(1, 1, n, d), rand(1, 1, n, d)
+    q, do = np.repeat(q1, G, axis=1), np.repeat(do1, G, axis=1)
+    _, dk, dv = oracle.attention_backward_gqa(q, k, v, do, 0.6)
+    _, dk1, dv1 = oracle.attention_backward(q1, k, v, do1, 0.6)
+    np.testing.assert_allclose(dk, G * dk1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dv, G * dv1, rtol=1e-13, atol=1e-14)
+
+
+def test_gqa_rejects_ragged_groups():
+    with pytest.raises(ValueError):
+        oracle.attention_forward_gqa(rand(1, 5, 4, 2), rand(1, 2, 4, 2), rand(1, 2, 4, 2), 1.0)
+
+
+# --------------------------------------------------------------------------
 # Backward: finite differences, closed forms, invariants
 # --------------------------------------------------------------------------
 
