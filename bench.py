@@ -7,9 +7,14 @@ H = 32, bf16, Q scaled by 3), inputs resident in device memory.  Throughput coun
 4*B*H*n^2*d (forward) + 10*B*H*n^2*d (backward), scaled by the fraction of
 (query, key) pairs a window lets through.
 
+The follow-on variants (grouped-query attention: K/V heads shared by groups
+of query heads, through the *_gqa entry points) are timed the same way after
+the main workload, with fewer steps, and reported under "variants".
+
 Prints ONE JSON line.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--cpu-seconds S] [--copy-calibration MIB]
+                  [--no-cpu-baseline] [--cpu-seconds S] [--no-variants]
+                  [--variant-steps K] [--copy-calibration MIB]
 
 --copy-calibration MIB also runs one plain device-to-device copy of MIB MiB
 after the timed steps; under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give
@@ -40,11 +45,13 @@ def flops(wl):
 
 def hbm_bytes(wl):
     """Algorithmic HBM bytes per call: fwd reads Q,K,V and writes O, LSE;
-    bwd reads Q,K,V,O,dO,LSE, writes dQ,dK,dV and writes+reads D."""
+    bwd reads Q,K,V,O,dO,LSE, writes dQ,dK,dV and writes+reads D.  K, V, dK
+    and dV have the workload's key/value head count."""
     eb = 2 if wl.dtype == "bf16" else 4
     t = wl.B * wl.H * wl.n * wl.d * eb
+    tkv = wl.B * wl.Hkv * wl.n * wl.d * eb
     r = wl.B * wl.H * wl.n * 4
-    return 4 * t + r, 8 * t + 3 * r
+    return 2 * t + 2 * tkv + r, 4 * t + 4 * tkv + 3 * r
 
 
 def measured_traffic(wl, kernel):
@@ -102,27 +109,20 @@ def cpu_baseline(wl, seconds):
                       f"{heads[-1]}, {t_total:.1f} s, BLAS threads={threads}, host cpus={os.cpu_count()}"}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
-    args = ap.parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the attention path runs on a single device); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        return 2
+def kernel_names(wl):
+    """Short names of the four kernels of a step: forward, rowdot, dK/dV, dQ."""
+    t, d = wl.dtype, wl.d
+    return [f"fwd_{t}_kernel<{d}>", f"bwd_rowdot_kernel<{d}>", f"bwd_kv_{t}_kernel<{d}>", f"bwd_q_{t}_kernel<{d}>"]
 
+
+def time_steps(wl, steps, warmup):
+    """Run `warmup` untimed and `steps` timed steps of the workload with its
+    inputs resident on the GPU; returns (per-kernel average ms [fwd, rowdot,
+    dK/dV, dQ], ms per step, wall seconds of the timed region)."""
     import torch
     import exact_attention_69_amd as ea
-    from workloads import draw_inputs, workload
+    from workloads import draw_inputs
 
-    wl = workload(args.workload)
-    fwd_f, bwd_f = flops(wl)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     x = draw_inputs(wl)
@@ -131,24 +131,23 @@ def main(argv=None):
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
     o = torch.empty_like(q)
     lse = torch.empty((wl.B, wl.H, wl.n), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     code = ea.EXATTN_BF16 if wl.dtype == "bf16" else ea.EXATTN_F32
     ws = torch.empty(max(ea.attn_bwd_workspace_bytes(code, wl.B, wl.H, wl.n, wl.d), 256), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    def fwd():
-        ea.attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream)
+    gqa = wl.Hkv != wl.H
+    attn_fwd = ea.attn_fwd_gqa if gqa else ea.attn_fwd
+    attn_bwd_dkdv = ea.attn_bwd_dkdv_gqa if gqa else ea.attn_bwd_dkdv
+    attn_bwd_dq = ea.attn_bwd_dq_gqa if gqa else ea.attn_bwd_dq
 
     # The backward runs as its three stage calls (the same three kernels that
     # attn_bwd launches), so that every kernel is bracketed by its own events.
-    def bwd_stages():
-        return (lambda: ea.attn_bwd_rowdot(o, do, workspace=ws, stream=stream),
-                lambda: ea.attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=stream),
-                lambda: ea.attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=stream))
-
-    calls = (fwd,) + bwd_stages()
-    for _ in range(args.warmup):
+    calls = (lambda: attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream),
+             lambda: ea.attn_bwd_rowdot(o, do, workspace=ws, stream=stream),
+             lambda: attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=stream),
+             lambda: attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=stream))
+    for _ in range(warmup):
         for c in calls:
             c()
     torch.cuda.synchronize()
@@ -156,12 +155,12 @@ def main(argv=None):
     # Whole steps, bracketed by device syncs, timed with events on the stream
     # the kernels are launched on; one event between consecutive kernels.
     nk = len(calls)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
-    for s in range(args.steps):
+    for s in range(steps):
         ev[s][0].record(stream)
         for i, c in enumerate(calls):
             c()
@@ -169,11 +168,35 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    kms = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / args.steps for i in range(nk)]
+    kms = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(nk)]
+    return kms, start.elapsed_time(end) / steps, wall
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--variant-steps", type=int, default=10)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the attention path runs on a single device); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    from workloads import VARIANTS, workload
+
+    wl = workload(args.workload)
+    fwd_f, bwd_f = flops(wl)
+    kms, ms, wall = time_steps(wl, args.steps, args.warmup)
+    nk = len(kms)
     fwd_ms = kms[0]
     bwd_ms = sum(kms[1:])
-    ms = total_ms / args.steps
     peak = PEAK_TFLOPS[wl.dtype]
     value = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
 
@@ -183,8 +206,7 @@ def main(argv=None):
     #   dQ pass       6*B*H*pairs*d  (S, dP, dQ = dS K)
     #   rowdot        memory bound (reads O and dO, writes D)
     kernel_flops = [fwd_f, None, 0.8 * bwd_f, 0.6 * bwd_f]
-    names = [f"fwd_bf16_kernel<{wl.d}>", f"bwd_rowdot_kernel<{wl.d}>", f"bwd_kv_bf16_kernel<{wl.d}>",
-             f"bwd_q_bf16_kernel<{wl.d}>"]
+    names = kernel_names(wl)
     dom = max(range(nk), key=lambda i: kms[i])
     ach = kernel_flops[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
@@ -192,7 +214,23 @@ def main(argv=None):
                 "algorithmic_flops_per_launch": kernel_flops[dom], "avg_launch_ms": round(kms[dom], 4)}
     fwd_tflops = fwd_f / (fwd_ms * 1e-3) / 1e12
 
+    variants = {}
+    if not args.no_variants:
+        for vw in VARIANTS:
+            vk, vms, _ = time_steps(vw, args.variant_steps, 3)
+            vf, vb = flops(vw)
+            vn = kernel_names(vw)
+            variants[vw.name] = {
+                "value": round((vf + vb) / (vms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(vms, 4),
+                "steps": args.variant_steps, "B": vw.B, "H": vw.H, "Hkv": vw.Hkv, "n": vw.n, "d": vw.d,
+                "window": vw.window, "kernel_ms": {vn[i]: round(vk[i], 4) for i in range(nk)},
+                "kernel_tflops": {vn[i]: round(f / (vk[i] * 1e-3) / 1e12, 2)
+                                  for i, f in enumerate([vf, None, 0.8 * vb, 0.6 * vb]) if f},
+                "hbm_gbs_algorithmic": round(sum(hbm_bytes(vw)) / (vms * 1e-3) / 1e9, 1)}
+
     if args.copy_calibration:
+        import torch
+        dev = torch.device("cuda:0")
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -217,6 +255,8 @@ def main(argv=None):
                    "bwd_hbm_gbs_algorithmic": round(hbm_bytes(wl)[1] / (bwd_ms * 1e-3) / 1e9, 1)},
         "roofline": roofline,
     }
+    if variants:
+        out["variants"] = variants
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -11,10 +11,14 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     attn_bwd,
     attn_bwd_dkdv,
+    attn_bwd_dkdv_gqa,
     attn_bwd_dq,
+    attn_bwd_dq_gqa,
+    attn_bwd_gqa,
     attn_bwd_rowdot,
     attn_bwd_workspace_bytes,
     attn_fwd,
+    attn_fwd_gqa,
     exattn_status_string,
     load_library,
 )

@@ -51,6 +51,14 @@ def load_library(path=None):
     lib.attn_bwd_dkdv.restype = ci
     lib.attn_bwd_dq.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, cs, vp]
     lib.attn_bwd_dq.restype = ci
+    lib.attn_fwd_gqa.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp, cf, ci, vp, vp, vp]
+    lib.attn_fwd_gqa.restype = ci
+    lib.attn_bwd_gqa.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, vp, cs, vp]
+    lib.attn_bwd_gqa.restype = ci
+    lib.attn_bwd_dkdv_gqa.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, cs, vp]
+    lib.attn_bwd_dkdv_gqa.restype = ci
+    lib.attn_bwd_dq_gqa.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, cs, vp]
+    lib.attn_bwd_dq_gqa.restype = ci
     lib.exattn_status_string.argtypes = [ci]
     lib.exattn_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -87,6 +95,26 @@ def _check_inputs(*ts):
             raise ValueError("Q, K, V (and O, dO) must share shape and dtype")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, n, d]")
+
+
+def _check_gqa(q, k, v, *qlike):
+    """Q (and O, dO) [B, H, n, d]; K, V [B, Hkv, n, d] with H % Hkv == 0.
+    Returns Hkv."""
+    _check_inputs(q, *qlike)
+    _check_inputs(k, v)
+    B, H, n, d = q.shape
+    Bk, Hkv, nk, dk = k.shape
+    if k.dtype != q.dtype or (Bk, nk, dk) != (B, n, d) or Hkv < 1 or H % Hkv:
+        raise ValueError(f"K/V shape {tuple(k.shape)} does not fit Q {tuple(q.shape)} "
+                         "(need [B, Hkv, n, d] with H a multiple of Hkv, same dtype)")
+    return Hkv
+
+
+def _call(fn, *args):
+    with _torch().cuda.device(args[-1][0]):
+        st = getattr(load_library(), fn)(*args[:-1], args[-1][1])
+    if st != 0:
+        raise ExattnError(fn, st, exattn_status_string(st))
 
 
 def _stream_ptr(t, stream):
@@ -204,4 +232,71 @@ def attn_bwd_dq(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, str
                                         _stream_ptr(q, stream))
     if st != 0:
         raise ExattnError("attn_bwd_dq", st, exattn_status_string(st))
+    return dq
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention: K, V (and dK, dV) have Hkv heads, Hkv dividing H.
+# ---------------------------------------------------------------------------
+
+def attn_fwd_gqa(q, k, v, scale=None, window=-1, out=None, lse=None, stream=None):
+    """Forward with Hkv = k.shape[1] key/value heads shared by groups of
+    H / Hkv consecutive query heads.  Returns (O like q, LSE float32 [B, H, n])."""
+    torch = _torch()
+    Hkv = _check_gqa(q, k, v)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    _call("attn_fwd_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale,
+          int(window), out.data_ptr(), lse.data_ptr(), (q.device, _stream_ptr(q, stream)))
+    return out, lse
+
+
+def attn_bwd_gqa(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None, dk=None, dv=None,
+                 stream=None):
+    """Backward of attn_fwd_gqa.  Returns (dQ like q, dK like k, dV like v);
+    dK and dV sum over each group's query heads."""
+    torch = _torch()
+    Hkv = _check_gqa(q, k, v, o, do)
+    _check_lse(lse, q)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    workspace, wsb = _workspace(q, code, workspace)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _call("attn_bwd_gqa", code, B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+          workspace.data_ptr(), wsb, (q.device, _stream_ptr(q, stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_dkdv_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dk=None, dv=None, stream=None):
+    """Backward stage 2 with shared key/value heads: dK, dV like k, v."""
+    torch = _torch()
+    Hkv = _check_gqa(q, k, v, do)
+    _check_lse(lse, q)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _call("attn_bwd_dkdv_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), scale, int(window), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+          workspace.numel() * workspace.element_size(), (q.device, _stream_ptr(q, stream)))
+    return dk, dv
+
+
+def attn_bwd_dq_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, stream=None):
+    """Backward stage 3 with shared key/value heads: dQ like q."""
+    torch = _torch()
+    Hkv = _check_gqa(q, k, v, do)
+    _check_lse(lse, q)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    _call("attn_bwd_dq_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), workspace.data_ptr(),
+          workspace.numel() * workspace.element_size(), (q.device, _stream_ptr(q, stream)))
     return dq

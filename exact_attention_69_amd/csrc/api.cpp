@@ -21,8 +21,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 size_t elem_bytes(int dtype) { return dtype == EXATTN_BF16 ? 2 : 4; }
 
 // Shape/scalar checks common to both passes.
-int check_problem(int dtype, int B, int H, int n, int d, float scale, int window) {
+int check_problem(int dtype, int B, int H, int n, int d, float scale, int window, int Hkv) {
   if (B < 1 || H < 1 || n < 1) return EXATTN_EINVAL;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return EXATTN_EINVAL;
   if (window < -1) return EXATTN_EINVAL;
   if (!isfinite(scale) || !(scale > 0.0f)) return EXATTN_EINVAL;
   if (dtype != EXATTN_F32 && dtype != EXATTN_BF16) return EXATTN_EUNSUPPORTED;
@@ -33,6 +34,11 @@ int check_problem(int dtype, int B, int H, int n, int d, float scale, int window
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_EHIP; }
+
+struct Span {
+  const void* p;
+  size_t n;
+};
 
 }  // namespace
 
@@ -49,29 +55,35 @@ const char* exattn_status_string(int status) {
   }
 }
 
-int attn_fwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
-             float scale, int window, void* O, float* LSE, void* stream) {
-  int st = check_problem(dtype, B, H, n, d, scale, window);
+int attn_fwd_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* Q, const void* K, const void* V,
+                 float scale, int window, void* O, float* LSE, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, window, Hkv);
   if (st != EXATTN_OK) return st;
   const void* ptrs[] = {Q, K, V, O, LSE};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return EXATTN_EINVAL;
-  size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
-  size_t lb = (size_t)B * H * n * sizeof(float);
-  const void* ins[] = {Q, K, V};
-  for (const void* in : ins) {
-    if (overlaps(O, tb, in, tb) || overlaps(LSE, lb, in, tb)) return EXATTN_EINVAL;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t kb = (size_t)B * Hkv * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const Span ins[] = {{Q, tb}, {K, kb}, {V, kb}};
+  for (const Span& in : ins) {
+    if (overlaps(O, tb, in.p, in.n) || overlaps(LSE, lb, in.p, in.n)) return EXATTN_EINVAL;
   }
   if (overlaps(O, tb, LSE, lb)) return EXATTN_EINVAL;
 
-  exattn::FwdParams p{Q, K, V, O, LSE, B, H, n, d, scale, window};
+  exattn::FwdParams p{Q, K, V, O, LSE, B, H, n, d, scale, window, H / Hkv};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == EXATTN_BF16 ? exattn::launch_fwd_bf16(p, s) : exattn::launch_fwd_f32(p, s);
   return from_hip(e);
 }
 
+int attn_fwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
+             float scale, int window, void* O, float* LSE, void* stream) {
+  return attn_fwd_gqa(dtype, B, H, H, n, d, Q, K, V, scale, window, O, LSE, stream);
+}
+
 size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d) {
-  if (check_problem(dtype, B, H, n, d, 1.0f, -1) != EXATTN_OK) return 0;
+  if (check_problem(dtype, B, H, n, d, 1.0f, -1, H) != EXATTN_OK) return 0;
   size_t rows = (size_t)B * H * n;
   return ((rows * sizeof(float) + 255) / 256) * 256;
 }
@@ -80,17 +92,12 @@ size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d) {
 
 namespace {
 
-struct Span {
-  const void* p;
-  size_t n;
-};
-
 // Validation shared by the backward entry points: every listed pointer is
 // non-null and 16-byte aligned, the workspace is large enough, no output
 // overlaps an input or another output.
-int check_bwd(int dtype, int B, int H, int n, int d, float scale, int window, const Span* ins, int nin,
+int check_bwd(int dtype, int B, int H, int Hkv, int n, int d, float scale, int window, const Span* ins, int nin,
               const Span* outs, int nout, size_t workspace_bytes) {
-  int st = check_problem(dtype, B, H, n, d, scale, window);
+  int st = check_problem(dtype, B, H, n, d, scale, window, Hkv);
   if (st != EXATTN_OK) return st;
   for (int i = 0; i < nin; ++i)
     if (ins[i].p == nullptr || !aligned16(ins[i].p)) return EXATTN_EINVAL;
@@ -116,68 +123,93 @@ int run_bwd(int dtype, const exattn::BwdParams& p, unsigned stages, void* stream
 
 extern "C" {
 
+int attn_bwd_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* LSE, float scale, int window, void* dQ, void* dK,
+                 void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, window, Hkv);
+  if (st != EXATTN_OK) return st;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t kb = (size_t)B * Hkv * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
+  const Span ins[] = {{Q, tb}, {K, kb}, {V, kb}, {O, tb}, {dO, tb}, {LSE, lb}};
+  const Span outs[] = {{dQ, tb}, {dK, kb}, {dV, kb}, {workspace, wb}};
+  st = check_bwd(dtype, B, H, Hkv, n, d, scale, window, ins, 6, outs, 4, workspace_bytes);
+  if (st != EXATTN_OK) return st;
+  exattn::BwdParams p{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, B, H, n, d, scale, window, H / Hkv};
+  return run_bwd(dtype, p, exattn::kStageAll, stream);
+}
+
 int attn_bwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
              const void* O, const void* dO, const float* LSE, float scale, int window, void* dQ,
              void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_problem(dtype, B, H, n, d, scale, window);
-  if (st != EXATTN_OK) return st;
-  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
-  const size_t lb = (size_t)B * H * n * sizeof(float);
-  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
-  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {O, tb}, {dO, tb}, {LSE, lb}};
-  const Span outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {workspace, wb}};
-  st = check_bwd(dtype, B, H, n, d, scale, window, ins, 6, outs, 4, workspace_bytes);
-  if (st != EXATTN_OK) return st;
-  exattn::BwdParams p{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, B, H, n, d, scale, window};
-  return run_bwd(dtype, p, exattn::kStageAll, stream);
+  return attn_bwd_gqa(dtype, B, H, H, n, d, Q, K, V, O, dO, LSE, scale, window, dQ, dK, dV, workspace,
+                      workspace_bytes, stream);
 }
 
 int attn_bwd_rowdot(int dtype, int B, int H, int n, int d, const void* O, const void* dO, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  int st = check_problem(dtype, B, H, n, d, 1.0f, -1);
+  int st = check_problem(dtype, B, H, n, d, 1.0f, -1, H);
   if (st != EXATTN_OK) return st;
   const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
   const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
   const Span ins[] = {{O, tb}, {dO, tb}};
   const Span outs[] = {{workspace, wb}};
-  st = check_bwd(dtype, B, H, n, d, 1.0f, -1, ins, 2, outs, 1, workspace_bytes);
+  st = check_bwd(dtype, B, H, H, n, d, 1.0f, -1, ins, 2, outs, 1, workspace_bytes);
   if (st != EXATTN_OK) return st;
   exattn::BwdParams p{nullptr, nullptr, nullptr, O, dO, nullptr, nullptr, nullptr, nullptr, (float*)workspace,
-                      B, H, n, d, 1.0f, -1};
+                      B, H, n, d, 1.0f, -1, 1};
   return run_bwd(dtype, p, exattn::kStageRowdot, stream);
+}
+
+int attn_bwd_dkdv_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* Q, const void* K,
+                      const void* V, const void* dO, const float* LSE, float scale, int window, void* dK, void* dV,
+                      const void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, window, Hkv);
+  if (st != EXATTN_OK) return st;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t kb = (size_t)B * Hkv * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
+  const Span ins[] = {{Q, tb}, {K, kb}, {V, kb}, {dO, tb}, {LSE, lb}, {workspace, wb}};
+  const Span outs[] = {{dK, kb}, {dV, kb}};
+  st = check_bwd(dtype, B, H, Hkv, n, d, scale, window, ins, 6, outs, 2, workspace_bytes);
+  if (st != EXATTN_OK) return st;
+  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, nullptr, dK, dV, (float*)workspace,
+                      B, H, n, d, scale, window, H / Hkv};
+  return run_bwd(dtype, p, exattn::kStageKV, stream);
 }
 
 int attn_bwd_dkdv(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
                   const void* dO, const float* LSE, float scale, int window, void* dK, void* dV,
                   const void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_problem(dtype, B, H, n, d, scale, window);
+  return attn_bwd_dkdv_gqa(dtype, B, H, H, n, d, Q, K, V, dO, LSE, scale, window, dK, dV, workspace,
+                           workspace_bytes, stream);
+}
+
+int attn_bwd_dq_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* Q, const void* K, const void* V,
+                    const void* dO, const float* LSE, float scale, int window, void* dQ, const void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, window, Hkv);
   if (st != EXATTN_OK) return st;
   const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t kb = (size_t)B * Hkv * n * d * elem_bytes(dtype);
   const size_t lb = (size_t)B * H * n * sizeof(float);
   const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
-  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {LSE, lb}, {workspace, wb}};
-  const Span outs[] = {{dK, tb}, {dV, tb}};
-  st = check_bwd(dtype, B, H, n, d, scale, window, ins, 6, outs, 2, workspace_bytes);
+  const Span ins[] = {{Q, tb}, {K, kb}, {V, kb}, {dO, tb}, {LSE, lb}, {workspace, wb}};
+  const Span outs[] = {{dQ, tb}};
+  st = check_bwd(dtype, B, H, Hkv, n, d, scale, window, ins, 6, outs, 1, workspace_bytes);
   if (st != EXATTN_OK) return st;
-  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, nullptr, dK, dV, (float*)workspace, B, H, n, d, scale, window};
-  return run_bwd(dtype, p, exattn::kStageKV, stream);
+  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, dQ, nullptr, nullptr, (float*)workspace,
+                      B, H, n, d, scale, window, H / Hkv};
+  return run_bwd(dtype, p, exattn::kStageQ, stream);
 }
 
 int attn_bwd_dq(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
                 const void* dO, const float* LSE, float scale, int window, void* dQ, const void* workspace,
                 size_t workspace_bytes, void* stream) {
-  int st = check_problem(dtype, B, H, n, d, scale, window);
-  if (st != EXATTN_OK) return st;
-  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
-  const size_t lb = (size_t)B * H * n * sizeof(float);
-  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
-  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {LSE, lb}, {workspace, wb}};
-  const Span outs[] = {{dQ, tb}};
-  st = check_bwd(dtype, B, H, n, d, scale, window, ins, 6, outs, 1, workspace_bytes);
-  if (st != EXATTN_OK) return st;
-  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, dQ, nullptr, nullptr, (float*)workspace, B, H, n, d, scale,
-                      window};
-  return run_bwd(dtype, p, exattn::kStageQ, stream);
+  return attn_bwd_dq_gqa(dtype, B, H, H, n, d, Q, K, V, dO, LSE, scale, window, dQ, workspace, workspace_bytes,
+                         stream);
 }
 
 }  // extern "C"

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int n, int n_kblocks, int total_blocks, float scale,
-    float scale_log2, int window) {
+    float scale_log2, int window, int group) {
   constexpr int NW = KvCfg<D>::NW;
   constexpr int BQ = KvCfg<D>::BQ;
   constexpr int NT = NW * 64;
@@ -54,15 +54,14 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE / D]
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
-  const int head = bid / n_kblocks;
-  const int kblk = bid - head * n_kblocks;
+  const int kvh = bid / n_kblocks;  // key/value head (batch-major)
+  const int kblk = bid - kvh * n_kblocks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
 
-  const size_t hoff = (size_t)head * n * D;
-  const __bf16* Q = Qg + hoff;
-  const __bf16* dO = dOg + hoff;
-  const float* lse = LSEg + (size_t)head * n;
-  const float* dl = Dg + (size_t)head * n;
+  // The group's query heads kvh*group .. kvh*group + group - 1 all attend to
+  // these keys: their contributions to dK and dV are summed in registers.
+  const size_t hoff = (size_t)kvh * n * D;
+  const int qh0 = kvh * group;
 
   const int kb0 = kblk * BKV;
   const int my_key = kb0 + wave * 32 + l32;
@@ -94,13 +93,15 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   // probabilities are masked to zero on the tail tile.
   using Tile = TileAsync<D, BQ, NT>;
   static_assert(BQ == 32, "the row-statistics copy maps 64 lanes to 2 x 32 rows");
-  auto load_tile = [&](int t, int buf) {
+  auto load_tile = [&](int t, int qg, int buf) {
     const int i0 = t * BQ;
-    Tile::issue(Q + (size_t)i0 * D, n - i0, tiles[buf][0], tid);
-    Tile::issue(dO + (size_t)i0 * D, n - i0, tiles[buf][1], tid);
+    // first row of the tile in [B*H*n]; B*H*n*D < 2^31 is checked at the ABI
+    const int qrow = (qh0 + qg) * n + i0;
+    Tile::issue(Qg + qrow * D, n - i0, tiles[buf][0], tid);
+    Tile::issue(dOg + qrow * D, n - i0, tiles[buf][1], tid);
     if (wave == 0) {  // lanes 0-31: LSE of rows i0.., lanes 32-63: D
-      const int i = min(i0 + l32, n - 1);
-      lds_dma4(hi ? (const void*)(dl + i) : (const void*)(lse + i), &rowst[buf][0][0]);
+      const int i = qrow + min(l32, n - 1 - i0);
+      lds_dma4(hi ? (const void*)(Dg + i) : (const void*)(LSEg + i), &rowst[buf][0][0]);
     }
   };
 
@@ -111,13 +112,21 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
     dv[i] = f32x16{};
   }
 
-  if (t_lo < t_hi) load_tile(t_lo, 0);
+  // One sweep over the band's query tiles per query head of the group.
+  const int steps = (t_hi - t_lo) * group;
+  if (steps > 0) load_tile(t_lo, 0, 0);
   wait_all_and_barrier();
 
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1, buf ^ 1);  // buffer released by the last barrier
+  int step = 0;
+  for (int qg = 0; qg < group; ++qg)
+  for (int t = t_lo; t < t_hi; ++t, ++step) {
+    const int buf = step & 1;
+    // prefetch the next tile (the next head's first tile after the last one);
+    // its buffer was released by the last barrier
+    if (t + 1 < t_hi)
+      load_tile(t + 1, qg, buf ^ 1);
+    else if (qg + 1 < group)
+      load_tile(t_lo, qg + 1, buf ^ 1);
     const __bf16* Qs = tiles[buf][0];
     const __bf16* dOs = tiles[buf][1];
     const int i0 = t * BQ;
@@ -209,7 +218,8 @@ template <int D, bool WINDOWED>
 __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
-    __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window) {
+    __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window,
+    int group) {
   constexpr int NW = QCfg<D>::NW;
   constexpr int BC = QCfg<D>::BC;
   constexpr int NT = NW * 64;
@@ -226,8 +236,9 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
 
   const size_t hoff = (size_t)head * n * D;
-  const __bf16* K = Kg + hoff;
-  const __bf16* V = Vg + hoff;
+  const size_t kv_off = (size_t)(head / group) * n * D;  // key/value head of this query head
+  const __bf16* K = Kg + kv_off;
+  const __bf16* V = Vg + kv_off;
   const int q0 = qb * BR;
   const int my_row = q0 + wave * 32 + l32;
 
@@ -339,9 +350,10 @@ template <int D, bool W>
 hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const float scale_log2 = p.scale * kLog2e;
   const long heads = (long)p.B * p.H;
+  const long kv_heads = heads / p.group;
   constexpr int BKV = 32 * KvCfg<D>::NW;
   const int nkb = (p.n + BKV - 1) / BKV;
-  const long tk = (long)nkb * heads;
+  const long tk = (long)nkb * kv_heads;
   constexpr int BR = 32 * QCfg<D>::NW;
   const int nqb = (p.n + BR - 1) / BR;
   const long tq = (long)nqb * heads;
@@ -354,14 +366,15 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   if (stages & kStageKV) {
     hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(KvCfg<D>::NW * 64), 0, stream,
                        (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
-                       p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window);
+                       p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window,
+                       p.group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageQ) {
     hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(QCfg<D>::NW * 64), 0, stream,
                        (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
-                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window);
+                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

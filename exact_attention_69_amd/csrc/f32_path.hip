@@ -40,7 +40,7 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
                                                       const float* __restrict__ Vg, float* __restrict__ Og,
                                                       float* __restrict__ LSEg, int n, int nqb, float scale,
-                                                      int window) {
+                                                      int window, int group) {
   constexpr int E = D / TPR;
   constexpr int TK = tile_rows<D>();
   __shared__ float Ks[TK][D];
@@ -49,8 +49,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
   const int row = qb * ROWS + rloc;
   const size_t hoff = (size_t)head * n * D;
-  const float* K = Kg + hoff;
-  const float* V = Vg + hoff;
+  const size_t kv_off = (size_t)(head / group) * n * D;  // shared key/value head
+  const float* K = Kg + kv_off;
+  const float* V = Vg + kv_off;
 
   float q[E], acc[E];
 #pragma unroll
@@ -118,20 +119,16 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
                                                          const float* __restrict__ Vg, const float* __restrict__ dOg,
                                                          const float* __restrict__ LSEg, const float* __restrict__ Dg,
                                                          float* __restrict__ dKg, float* __restrict__ dVg, int n,
-                                                         int nkb, float scale, int window) {
+                                                         int nkb, float scale, int window, int group) {
   constexpr int E = D / TPR;
   constexpr int TK = tile_rows<D>();
   __shared__ float Qs[TK][D];
   __shared__ float dOs[TK][D];
   __shared__ float Ls[TK], Ds[TK];
-  const int head = blockIdx.x / nkb, kb = blockIdx.x - (blockIdx.x / nkb) * nkb;
+  const int kvh = blockIdx.x / nkb, kb = blockIdx.x - (blockIdx.x / nkb) * nkb;  // key/value head, key block
   const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
   const int key = kb * ROWS + rloc;
-  const size_t hoff = (size_t)head * n * D;
-  const float* Q = Qg + hoff;
-  const float* dO = dOg + hoff;
-  const float* lse = LSEg + (size_t)head * n;
-  const float* dl = Dg + (size_t)head * n;
+  const size_t hoff = (size_t)kvh * n * D;
 
   float k[E], v[E], dk[E], dv[E];
 #pragma unroll
@@ -148,37 +145,45 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
   int row_lo = 0, row_hi = n;
   band_keys(key, key + 1, n, window, &row_lo, &row_hi);
   const unsigned row_span = key < n ? (unsigned)max(row_hi - row_lo, 0) : 0u;
-  for (int i0 = (q_lo / TK) * TK; i0 < q_hi; i0 += TK) {
-    __syncthreads();
-    for (int i = tid; i < TK * D; i += 256) {
-      const int r = i / D, c = i - (i / D) * D;
-      const bool ok = i0 + r < n;
-      Qs[r][c] = ok ? Q[(size_t)(i0 + r) * D + c] : 0.0f;
-      dOs[r][c] = ok ? dO[(size_t)(i0 + r) * D + c] : 0.0f;
-    }
-    if (tid < TK) {
-      const bool ok = i0 + tid < n;
-      Ls[tid] = ok ? lse[i0 + tid] : 0.0f;
-      Ds[tid] = ok ? dl[i0 + tid] : 0.0f;
-    }
-    __syncthreads();
-    for (int r = 0; r < TK; ++r) {
-      const int qi = i0 + r;
-      float ps = 0.0f, pd = 0.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        ps = fmaf(k[e], Qs[r][TPR * e + sub], ps);
-        pd = fmaf(v[e], dOs[r][TPR * e + sub], pd);
+  // dK and dV sum over the group's query heads kvh*group .. kvh*group + group - 1.
+  for (int qg = 0; qg < group; ++qg) {
+    const size_t qh = (size_t)kvh * group + qg;
+    const float* Q = Qg + qh * n * D;
+    const float* dO = dOg + qh * n * D;
+    const float* lse = LSEg + qh * n;
+    const float* dl = Dg + qh * n;
+    for (int i0 = (q_lo / TK) * TK; i0 < q_hi; i0 += TK) {
+      __syncthreads();
+      for (int i = tid; i < TK * D; i += 256) {
+        const int r = i / D, c = i - (i / D) * D;
+        const bool ok = i0 + r < n;
+        Qs[r][c] = ok ? Q[(size_t)(i0 + r) * D + c] : 0.0f;
+        dOs[r][c] = ok ? dO[(size_t)(i0 + r) * D + c] : 0.0f;
       }
-      const float sc = row_sum8(ps) * scale;
-      const float dp = row_sum8(pd);
-      const bool live = (unsigned)(qi - row_lo) < row_span;
-      const float p = live ? expf(sc - Ls[r]) : 0.0f;
-      const float ds = p * (dp - Ds[r]) * scale;
+      if (tid < TK) {
+        const bool ok = i0 + tid < n;
+        Ls[tid] = ok ? lse[i0 + tid] : 0.0f;
+        Ds[tid] = ok ? dl[i0 + tid] : 0.0f;
+      }
+      __syncthreads();
+      for (int r = 0; r < TK; ++r) {
+        const int qi = i0 + r;
+        float ps = 0.0f, pd = 0.0f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        dv[e] = fmaf(p, dOs[r][TPR * e + sub], dv[e]);
-        dk[e] = fmaf(ds, Qs[r][TPR * e + sub], dk[e]);
+        for (int e = 0; e < E; ++e) {
+          ps = fmaf(k[e], Qs[r][TPR * e + sub], ps);
+          pd = fmaf(v[e], dOs[r][TPR * e + sub], pd);
+        }
+        const float sc = row_sum8(ps) * scale;
+        const float dp = row_sum8(pd);
+        const bool live = (unsigned)(qi - row_lo) < row_span;
+        const float p = live ? expf(sc - Ls[r]) : 0.0f;
+        const float ds = p * (dp - Ds[r]) * scale;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          dv[e] = fmaf(p, dOs[r][TPR * e + sub], dv[e]);
+          dk[e] = fmaf(ds, Qs[r][TPR * e + sub], dk[e]);
+        }
       }
     }
   }
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
                                                         const float* __restrict__ Vg, const float* __restrict__ dOg,
                                                         const float* __restrict__ LSEg, const float* __restrict__ Dg,
                                                         float* __restrict__ dQg, int n, int nqb, float scale,
-                                                        int window) {
+                                                        int window, int group) {
   constexpr int E = D / TPR;
   constexpr int TK = tile_rows<D>();
   __shared__ float Ks[TK][D];
@@ -208,8 +213,9 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
   const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
   const int row = qb * ROWS + rloc;
   const size_t hoff = (size_t)head * n * D;
-  const float* K = Kg + hoff;
-  const float* V = Vg + hoff;
+  const size_t kv_off = (size_t)(head / group) * n * D;  // shared key/value head
+  const float* K = Kg + kv_off;
+  const float* V = Vg + kv_off;
 
   float q[E], g[E], dq[E];
 #pragma unroll
@@ -265,7 +271,8 @@ hipError_t fwd_d(const FwdParams& p, hipStream_t stream) {
   const long total = (long)nqb * p.B * p.H;
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
-                     (const float*)p.k, (const float*)p.v, (float*)p.o, p.lse, p.n, nqb, p.scale, p.window);
+                     (const float*)p.k, (const float*)p.v, (float*)p.o, p.lse, p.n, nqb, p.scale, p.window,
+                     p.group);
   return hipGetLastError();
 }
 
@@ -273,6 +280,7 @@ template <int D>
 hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const int nb = (p.n + ROWS - 1) / ROWS;
   const long total = (long)nb * p.B * p.H;
+  const long total_kv = total / p.group;  // key blocks: one set per key/value head
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
   if (stages & kStageRowdot) {
     hipError_t e = launch_rowdot<float>((const float*)p.o, (const float*)p.dout, p.delta, (long)p.B * p.H * p.n, D,
@@ -280,16 +288,16 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stages & kStageKV) {
-    hipLaunchKernelGGL((bwd_kv_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
+    hipLaunchKernelGGL((bwd_kv_f32_kernel<D>), dim3((unsigned)total_kv), dim3(256), 0, stream, (const float*)p.q,
                        (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dk,
-                       (float*)p.dv, p.n, nb, p.scale, p.window);
+                       (float*)p.dv, p.n, nb, p.scale, p.window, p.group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageQ) {
     hipLaunchKernelGGL((bwd_q_f32_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, (const float*)p.q,
                        (const float*)p.k, (const float*)p.v, (const float*)p.dout, p.lse, p.delta, (float*)p.dq,
-                       p.n, nb, p.scale, p.window);
+                       p.n, nb, p.scale, p.window, p.group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

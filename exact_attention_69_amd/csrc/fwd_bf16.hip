@@ -60,7 +60,7 @@ template <int D, bool WINDOWED>
 __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n_qblocks, int total_blocks,
-    float scale_log2, int window) {
+    float scale_log2, int window, int group) {
   constexpr int NW = FwdCfg<D>::NW;
   constexpr int RB = FwdCfg<D>::RB;
   constexpr int BC = FwdCfg<D>::BC;
@@ -83,10 +83,13 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
+  // Query heads [g*group, (g+1)*group) share key/value head g; consecutive
+  // logical blocks of one group land on the same XCD and share its L2.
   const size_t head_off = (size_t)head * n * D;
+  const size_t kv_off = (size_t)(head / group) * n * D;
   const __bf16* Q = Qg + head_off;
-  const __bf16* K = Kg + head_off;
-  const __bf16* V = Vg + head_off;
+  const __bf16* K = Kg + kv_off;
+  const __bf16* V = Vg + kv_off;
 
   const int q0 = qb * BR;
   const int w0 = q0 + wave * 32 * RB;  // first row of this wave
@@ -310,7 +313,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   const float scale_log2 = p.scale * kLog2e;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, W>), dim3((unsigned)total), dim3(FwdCfg<D>::NW * 64), 0, stream,
                      (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (__bf16*)p.o, p.lse, p.n,
-                     nqb, (int)total, scale_log2, p.window);
+                     nqb, (int)total, scale_log2, p.window, p.group);
   return hipGetLastError();
 }
 

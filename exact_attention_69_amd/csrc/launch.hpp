@@ -15,6 +15,7 @@ struct FwdParams {
   int B, H, n, d;
   float scale;
   int window;  // -1: no mask
+  int group;   // query heads per key/value head: K, V are [B, H / group, n, d]
 };
 
 struct BwdParams {
@@ -31,6 +32,7 @@ struct BwdParams {
   int B, H, n, d;
   float scale;
   int window;
+  int group;  // query heads per key/value head: K, V, dK, dV are [B, H / group, n, d]
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);

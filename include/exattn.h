@@ -28,10 +28,20 @@
  *                symmetric and inclusive).  Key tiles that lie wholly outside
  *                a query tile's band are skipped, not computed.
  *
+ * Grouped-query and multi-query attention (the *_gqa entry points)
+ *   The attention variants the unite.ai page lists under "FlashAttention-2"
+ *   (item 3): Hkv key/value heads, each shared by G = H / Hkv consecutive
+ *   query heads.  Query head h of batch b attends with key/value head
+ *   h / G of batch b; Hkv = 1 is multi-query attention and Hkv = H the plain
+ *   multi-head case (the entry points without the suffix are exactly that).
+ *   The gradient of a shared key/value head is the sum over its G query heads.
+ *
  * Layout and types (all tensors are DEVICE pointers)
  *   Q, K, V, O, dO, dQ, dK, dV : contiguous row-major [B, H, n, d]; element
  *                                type `dtype` (EXATTN_F32 = float,
  *                                EXATTN_BF16 = bfloat16 bit patterns).
+ *                                In the *_gqa calls K, V, dK, dV are
+ *                                [B, Hkv, n, d].
  *   LSE                        : contiguous [B, H, n], float32, natural log.
  *   workspace                  : device scratch owned by the caller, at least
  *                                attn_bwd_workspace_bytes() bytes.
@@ -50,7 +60,8 @@
  *   output or workspace buffer must be ordered by the caller.
  *
  * Errors (no exception crosses the ABI; nothing is launched on error)
- *   EXATTN_EINVAL       null pointer, B/H/n < 1, window < -1, non-finite or
+ *   EXATTN_EINVAL       null pointer, B/H/n < 1, Hkv < 1 or not dividing H,
+ *                       window < -1, non-finite or
  *                       non-positive scale, a pointer not 16-byte aligned,
  *                       an output buffer overlapping an input buffer, or a
  *                       problem of 2^31 elements or more per tensor.
@@ -158,6 +169,46 @@ int attn_bwd_dq(int dtype, int B, int H, int n, int d,
                 void *dQ,
                 const void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/*
+ * Grouped-query variants: as attn_fwd, attn_bwd, attn_bwd_dkdv and
+ * attn_bwd_dq, with Hkv key/value heads (1 <= Hkv <= H, H % Hkv == 0);
+ * K, V, dK and dV are [B, Hkv, n, d], everything else keeps its [B, H, ...]
+ * shape.  The workspace is the same as for H heads
+ * (attn_bwd_workspace_bytes(dtype, B, H, n, d)), and attn_bwd_rowdot serves
+ * as stage 1 unchanged.  attn_bwd_dkdv_gqa writes each dK/dV row once: the
+ * workgroup that owns a block of keys sweeps the query tiles of all G query
+ * heads of the group, so the group sum needs no atomics.
+ */
+int attn_fwd_gqa(int dtype, int B, int H, int Hkv, int n, int d,
+                 const void *Q, const void *K, const void *V,
+                 float scale, int window,
+                 void *O, float *LSE,
+                 void *stream);
+
+int attn_bwd_gqa(int dtype, int B, int H, int Hkv, int n, int d,
+                 const void *Q, const void *K, const void *V,
+                 const void *O, const void *dO, const float *LSE,
+                 float scale, int window,
+                 void *dQ, void *dK, void *dV,
+                 void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+int attn_bwd_dkdv_gqa(int dtype, int B, int H, int Hkv, int n, int d,
+                      const void *Q, const void *K, const void *V,
+                      const void *dO, const float *LSE,
+                      float scale, int window,
+                      void *dK, void *dV,
+                      const void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+int attn_bwd_dq_gqa(int dtype, int B, int H, int Hkv, int n, int d,
+                    const void *Q, const void *K, const void *V,
+                    const void *dO, const float *LSE,
+                    float scale, int window,
+                    void *dQ,
+                    const void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *exattn_status_string(int status);

@@ -15,9 +15,10 @@ BF16_LSE_MAX_REL = 2e-2
 BF16_GRAD_FRO_REL = 3e-2
 
 
-def make_case(B, H, n, d, dtype, window=-1, q_mult=1.0, seed=12345):
-    return Workload(f"case_b{B}h{H}n{n}d{d}_{dtype}_w{window}", B, H, n, d, dtype, window=window,
-                    q_mult=q_mult, seed=seed)
+def make_case(B, H, n, d, dtype, window=-1, q_mult=1.0, seed=12345, kv_heads=0):
+    kv = f"kv{kv_heads}" if kv_heads else ""
+    return Workload(f"case_b{B}h{H}{kv}n{n}d{d}_{dtype}_w{window}", B, H, n, d, dtype, window=window,
+                    q_mult=q_mult, seed=seed, kv_heads=kv_heads)
 
 
 def to_device(arrs, dtype):
@@ -73,19 +74,32 @@ def run_gpu(wl, inputs, backward=True):
     import torch
     import exact_attention_69_amd as ea
     t = to_device(inputs, wl.dtype)
-    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale, wl.window)
+    gqa = wl.Hkv != wl.H
+    fwd, bwd = (ea.attn_fwd_gqa, ea.attn_bwd_gqa) if gqa else (ea.attn_fwd, ea.attn_bwd)
+    o, lse = fwd(t["q"], t["k"], t["v"], wl.scale, wl.window)
     out = {"o": o, "lse": lse}
     if backward:
-        dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, wl.scale, wl.window)
+        dq, dk, dv = bwd(t["q"], t["k"], t["v"], o, t["do"], lse, wl.scale, wl.window)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {k: v.float().cpu().numpy() for k, v in out.items()}
 
 
 def oracle_case(wl, inputs, heads=None):
-    """Full oracle on all heads (or on the listed flat head indices)."""
+    """Full oracle on all heads (or on the listed flat head indices; with
+    shared key/value heads, on the listed flat key/value heads together with
+    all query heads of their groups)."""
     import oracle
     q, k, v, do = (inputs[x] for x in ("q", "k", "v", "do"))
+    if wl.Hkv != wl.H:
+        G = wl.group
+        if heads is not None:
+            qsel = lambda a: a.reshape(-1, G, wl.n, wl.d)[heads]
+            ksel = lambda a: a.reshape(-1, 1, wl.n, wl.d)[heads]
+            q, do, k, v = qsel(q), qsel(do), ksel(k), ksel(v)
+        O, lse = oracle.attention_forward_gqa(q, k, v, wl.scale, wl.window)
+        dq, dk, dv = oracle.attention_backward_gqa(q, k, v, do, wl.scale, wl.window)
+        return {"o": O, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
     if heads is not None:
         sel = lambda a: a.reshape(-1, wl.n, wl.d)[heads]
         q, k, v, do = sel(q), sel(k), sel(v), sel(do)
@@ -95,22 +109,32 @@ def oracle_case(wl, inputs, heads=None):
 
 
 def select_heads(outs, wl, heads):
+    """The outputs of the flat heads ``heads`` in the layout oracle_case
+    returns for them (with shared key/value heads: key/value heads, each with
+    its group of query heads)."""
     res = {}
+    G = wl.group
     for key, a in outs.items():
         if key == "lse":
-            res[key] = a.reshape(-1, wl.n)[heads]
-        else:
+            res[key] = a.reshape(-1, G, wl.n)[heads] if G > 1 else a.reshape(-1, wl.n)[heads]
+        elif key in ("dk", "dv") or G == 1:
             res[key] = a.reshape(-1, wl.n, wl.d)[heads]
+            if G > 1:
+                res[key] = res[key][:, None]
+        else:
+            res[key] = a.reshape(-1, G, wl.n, wl.d)[heads]
     return res
 
 
 def invariant_errors(inputs, outs, wl):
-    """Whole-tensor identities of the exact gradients, per head, as ratios:
-    sum_j dK_j = 0; sum_j dV_j = sum_i dO_i; <dQ,Q> = <dK,K>."""
-    q = inputs["q"].reshape(-1, wl.n, wl.d).astype(np.float64)
+    """Whole-tensor identities of the exact gradients, per key/value head, as
+    ratios: sum_j dK_j = 0; sum_j dV_j = sum of dO over the rows of the
+    group's query heads; sum over the group of <dQ,Q> = <dK,K>."""
+    G = wl.group
+    q = inputs["q"].reshape(-1, G * wl.n, wl.d).astype(np.float64)
     k = inputs["k"].reshape(-1, wl.n, wl.d).astype(np.float64)
-    do = inputs["do"].reshape(-1, wl.n, wl.d).astype(np.float64)
-    dq = outs["dq"].reshape(-1, wl.n, wl.d).astype(np.float64)
+    do = inputs["do"].reshape(-1, G * wl.n, wl.d).astype(np.float64)
+    dq = outs["dq"].reshape(-1, G * wl.n, wl.d).astype(np.float64)
     dk = outs["dk"].reshape(-1, wl.n, wl.d).astype(np.float64)
     dv = outs["dv"].reshape(-1, wl.n, wl.d).astype(np.float64)
     sum_dk = np.linalg.norm(dk.sum(axis=1), axis=-1) / np.maximum(np.linalg.norm(dk, axis=-1).sum(axis=1), 1e-30)

@@ -36,8 +36,16 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rowdot",
-                                    "attn_bwd_workspace_bytes", "attn_fwd", "exattn_status_string"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dkdv_gqa", "attn_bwd_dq",
+                                    "attn_bwd_dq_gqa", "attn_bwd_gqa", "attn_bwd_rowdot",
+                                    "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_gqa",
+                                    "exattn_status_string"]
+
+
+def test_binding_wraps_every_declared_symbol():
+    import exact_attention_69_amd as ea
+    for name in declared_functions():
+        assert callable(getattr(ea, name)), name
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -140,6 +148,36 @@ def test_backward_stages_reject_bad_arguments(lib):
     assert lib.attn_bwd_dq(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, dk, ws, need - 1, None) == EWORKSPACE
     assert lib.attn_bwd_dq(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, k, ws, need, None) == EINVAL
     assert lib.attn_bwd_dq(1, 1, 1, 128, 64, q, k, v, do, None, 0.1, -1, dk, ws, need, None) == EINVAL
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 0), (4, -1), (4, 3), (4, 8), (6, 4)])
+def test_gqa_rejects_bad_group(lib, H, Hkv):
+    q, k, v, o, lse = ptrs(5)
+    assert lib.attn_fwd_gqa(1, 1, H, Hkv, 128, 64, q, k, v, 0.1, -1, o, lse, None) == EINVAL
+    need = lib.attn_bwd_workspace_bytes(1, 1, H, 128, 64)
+    q, k, v, o, do, lse, dq, dk, dv, ws = ptrs(10)
+    assert lib.attn_bwd_gqa(1, 1, H, Hkv, 128, 64, q, k, v, o, do, lse, 0.1, -1, dq, dk, dv, ws, need,
+                            None) == EINVAL
+    assert lib.attn_bwd_dkdv_gqa(1, 1, H, Hkv, 128, 64, q, k, v, do, lse, 0.1, -1, dk, dv, ws, need,
+                                 None) == EINVAL
+    assert lib.attn_bwd_dq_gqa(1, 1, H, Hkv, 128, 64, q, k, v, do, lse, 0.1, -1, dq, ws, need, None) == EINVAL
+
+
+def test_gqa_overlap_checks_use_the_kv_size(lib):
+    # With H = 8, Hkv = 2, n = 128, d = 64 bf16, K is 32 KiB: an output placed
+    # 16 KiB after K overlaps it, one placed 32 KiB after does not (the call
+    # then fails later, on the undersized workspace, not on the overlap).
+    H, Hkv, n, d = 8, 2, 128, 64
+    kb = Hkv * n * d * 2
+    q, k, v, o, do, lse, dq, dv, ws = ptrs(9)
+    need = lib.attn_bwd_workspace_bytes(1, 1, H, n, d)
+    inside = ctypes.c_void_p(k.value + kb // 2)
+    after = ctypes.c_void_p(k.value + kb)
+    assert lib.attn_bwd_gqa(1, 1, H, Hkv, n, d, q, k, v, o, do, lse, 0.1, -1, dq, inside, dv, ws, need,
+                            None) == EINVAL
+    assert lib.attn_bwd_gqa(1, 1, H, Hkv, n, d, q, k, v, o, do, lse, 0.1, -1, dq, after, dv, ws, need - 1,
+                            None) == EWORKSPACE
+    assert lib.attn_fwd_gqa(1, 1, H, Hkv, n, d, q, k, v, 0.1, -1, inside, lse, None) == EINVAL
 
 
 def test_binding_rejects_host_tensors():

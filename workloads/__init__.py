@@ -14,6 +14,8 @@ on its own without drawing the whole problem):
 * rounding: for bf16 workloads the float32 values are rounded to bf16 with
   round-to-nearest-even and kept as float32 (exactly representable), so the
   oracle upcasts the very values the GPU receives.
+* grouped-query workloads (``kv_heads`` < H): K and V are drawn for heads
+  ``h < kv_heads`` only, with the same per-(b, h) streams.
 """
 
 from dataclasses import dataclass, field
@@ -23,6 +25,7 @@ import numpy as np
 __all__ = [
     "Workload",
     "WORKLOADS",
+    "VARIANTS",
     "workload",
     "round_to_bf16",
     "draw_head",
@@ -35,7 +38,8 @@ TENSORS = ("q", "k", "v", "do")
 
 @dataclass(frozen=True)
 class Workload:
-    """One problem shape: [B, H, n, d] tensors, element type, window."""
+    """One problem shape: Q, O, dO [B, H, n, d]; K, V [B, Hkv, n, d]
+    (Hkv = ``kv_heads``, 0 meaning H); element type, window."""
 
     name: str
     B: int
@@ -46,6 +50,7 @@ class Workload:
     window: int = -1  # -1: no mask; w >= 0: |i - j| <= w
     q_mult: float = 1.0
     seed: int = 69000
+    kv_heads: int = 0  # 0: one key/value head per query head
     note: str = field(default="", compare=False)
 
     @property
@@ -53,8 +58,19 @@ class Workload:
         return float(1.0 / np.sqrt(self.d))
 
     @property
+    def Hkv(self):
+        return self.kv_heads or self.H
+
+    @property
+    def group(self):
+        return self.H // self.Hkv
+
+    @property
     def shape(self):
         return (self.B, self.H, self.n, self.d)
+
+    def tensor_shape(self, tensor):
+        return (self.B, self.Hkv, self.n, self.d) if tensor in ("k", "v") else self.shape
 
 
 WORKLOADS = [
@@ -69,12 +85,18 @@ WORKLOADS = [
              seed=69005, note="Longformer-style local window |i-j|<=512"),
 ]
 
+# Follow-on variants, measured beside the workloads above.
+VARIANTS = [
+    Workload("bf16_b2h32kv8_n8192_d128_gqa", 2, 32, 8192, 128, "bf16", seed=69006, kv_heads=8,
+             note="grouped-query: 8 key/value heads, each shared by 4 query heads"),
+]
+
 
 def workload(name_or_index):
     """Look a workload up by name or by its position in ``WORKLOADS``."""
     if isinstance(name_or_index, int):
         return WORKLOADS[name_or_index]
-    for w in WORKLOADS:
+    for w in WORKLOADS + VARIANTS:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)
@@ -106,14 +128,16 @@ def draw_head(wl, tensor, b, h, n=None, d=None):
 
 
 def draw_inputs(wl, tensors=TENSORS, heads=None):
-    """Dict of float32 arrays [B, H, n, d] (or [len(heads), n, d] if ``heads``
-    lists (b, h) pairs) for the requested tensors."""
+    """Dict of float32 arrays [B, H, n, d] ([B, Hkv, n, d] for K and V; or
+    [len(heads), n, d] if ``heads`` lists (b, h) pairs) for the requested
+    tensors."""
     out = {}
     for name in tensors:
         if heads is None:
-            arr = np.empty(wl.shape, dtype=np.float32)
-            for b in range(wl.B):
-                for h in range(wl.H):
+            shape = wl.tensor_shape(name)
+            arr = np.empty(shape, dtype=np.float32)
+            for b in range(shape[0]):
+                for h in range(shape[1]):
                     arr[b, h] = draw_head(wl, name, b, h)
         else:
             arr = np.stack([draw_head(wl, name, b, h) for (b, h) in heads])
