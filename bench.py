@@ -144,7 +144,7 @@ def time_steps(wl, steps, warmup):
     # The backward runs as its three stage calls (the same three kernels that
     # attn_bwd launches), so that every kernel is bracketed by its own events.
     calls = (lambda: attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream),
-             lambda: ea.attn_bwd_rowdot(o, do, workspace=ws, stream=stream),
+             lambda: ea.attn_bwd_rowdot(o, do, lse, workspace=ws, stream=stream),
              lambda: attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=stream),
              lambda: attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=stream))
     for _ in range(warmup):
@@ -204,7 +204,7 @@ def main(argv=None):
     #   forward       4*B*H*pairs*d  (S = Q K^T and O = P V)
     #   dK/dV pass    8*B*H*pairs*d  (S, dP = dO V^T, dV = P^T dO, dK = dS^T Q)
     #   dQ pass       6*B*H*pairs*d  (S, dP, dQ = dS K)
-    #   rowdot        memory bound (reads O and dO, writes D)
+    #   rowdot        memory bound (reads O, dO and LSE, writes D and LSE*log2e)
     kernel_flops = [fwd_f, None, 0.8 * bwd_f, 0.6 * bwd_f]
     names = kernel_names(wl)
     dom = max(range(nk), key=lambda i: kms[i])

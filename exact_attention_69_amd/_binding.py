@@ -45,7 +45,7 @@ def load_library(path=None):
     lib.attn_bwd_workspace_bytes.restype = cs
     lib.attn_bwd.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, vp, cs, vp]
     lib.attn_bwd.restype = ci
-    lib.attn_bwd_rowdot.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, cs, vp]
+    lib.attn_bwd_rowdot.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, cs, vp]
     lib.attn_bwd_rowdot.restype = ci
     lib.attn_bwd_dkdv.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, cs, vp]
     lib.attn_bwd_dkdv.restype = ci
@@ -183,16 +183,18 @@ def _workspace(q, code, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def attn_bwd_rowdot(o, do, workspace=None, stream=None):
-    """Backward stage 1: D = rowsum(dO * O) into the workspace (returned)."""
+def attn_bwd_rowdot(o, do, lse, workspace=None, stream=None):
+    """Backward stage 1: D = rowsum(dO * O) and LSE*log2(e) into the workspace
+    (returned)."""
     torch = _torch()
     _check_inputs(o, do)
+    _check_lse(lse, o)
     B, H, n, d = o.shape
     code = _dtype_code(o)
     workspace, wsb = _workspace(o, code, workspace)
     with torch.cuda.device(o.device):
-        st = load_library().attn_bwd_rowdot(code, B, H, n, d, o.data_ptr(), do.data_ptr(), workspace.data_ptr(),
-                                            wsb, _stream_ptr(o, stream))
+        st = load_library().attn_bwd_rowdot(code, B, H, n, d, o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                            workspace.data_ptr(), wsb, _stream_ptr(o, stream))
     if st != 0:
         raise ExattnError("attn_bwd_rowdot", st, exattn_status_string(st))
     return workspace

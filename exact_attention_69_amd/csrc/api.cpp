@@ -82,10 +82,16 @@ int attn_fwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K
   return attn_fwd_gqa(dtype, B, H, H, n, d, Q, K, V, scale, window, O, LSE, stream);
 }
 
+// Workspace layout: [D: B*H*n fp32][LSE*log2(e): B*H*n fp32], each region
+// starting on a 256-byte boundary.
+static size_t ws_region_bytes(int B, int H, int n) {
+  const size_t rows = (size_t)B * H * n;
+  return ((rows * sizeof(float) + 255) / 256) * 256;
+}
+
 size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d) {
   if (check_problem(dtype, B, H, n, d, 1.0f, -1, H) != EXATTN_OK) return 0;
-  size_t rows = (size_t)B * H * n;
-  return ((rows * sizeof(float) + 255) / 256) * 256;
+  return 2 * ws_region_bytes(B, H, n);
 }
 
 }  // extern "C"
@@ -113,6 +119,14 @@ int check_bwd(int dtype, int B, int H, int Hkv, int n, int d, float scale, int w
   return EXATTN_OK;
 }
 
+exattn::BwdParams bwd_params(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, void* dQ, void* dK, void* dV, const void* workspace, int B, int H,
+                             int n, int d, float scale, int window, int group) {
+  float* ws = (float*)workspace;
+  float* lse2 = (float*)((char*)workspace + ws_region_bytes(B, H, n));
+  return exattn::BwdParams{Q, K, V, O, dO, LSE, dQ, dK, dV, ws, lse2, B, H, n, d, scale, window, group};
+}
+
 int run_bwd(int dtype, const exattn::BwdParams& p, unsigned stages, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == EXATTN_BF16 ? exattn::launch_bwd_bf16(p, stages, s) : exattn::launch_bwd_f32(p, stages, s);
@@ -136,8 +150,8 @@ int attn_bwd_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* Q, 
   const Span outs[] = {{dQ, tb}, {dK, kb}, {dV, kb}, {workspace, wb}};
   st = check_bwd(dtype, B, H, Hkv, n, d, scale, window, ins, 6, outs, 4, workspace_bytes);
   if (st != EXATTN_OK) return st;
-  exattn::BwdParams p{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, B, H, n, d, scale, window, H / Hkv};
-  return run_bwd(dtype, p, exattn::kStageAll, stream);
+  return run_bwd(dtype, bwd_params(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, n, d, scale, window, H / Hkv),
+                 exattn::kStageAll, stream);
 }
 
 int attn_bwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
@@ -147,19 +161,21 @@ int attn_bwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K
                       workspace_bytes, stream);
 }
 
-int attn_bwd_rowdot(int dtype, int B, int H, int n, int d, const void* O, const void* dO, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int attn_bwd_rowdot(int dtype, int B, int H, int n, int d, const void* O, const void* dO, const float* LSE,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_problem(dtype, B, H, n, d, 1.0f, -1, H);
   if (st != EXATTN_OK) return st;
   const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
   const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
-  const Span ins[] = {{O, tb}, {dO, tb}};
+  const Span ins[] = {{O, tb}, {dO, tb}, {LSE, lb}};
   const Span outs[] = {{workspace, wb}};
-  st = check_bwd(dtype, B, H, H, n, d, 1.0f, -1, ins, 2, outs, 1, workspace_bytes);
+  st = check_bwd(dtype, B, H, H, n, d, 1.0f, -1, ins, 3, outs, 1, workspace_bytes);
   if (st != EXATTN_OK) return st;
-  exattn::BwdParams p{nullptr, nullptr, nullptr, O, dO, nullptr, nullptr, nullptr, nullptr, (float*)workspace,
-                      B, H, n, d, 1.0f, -1, 1};
-  return run_bwd(dtype, p, exattn::kStageRowdot, stream);
+  return run_bwd(dtype,
+                 bwd_params(nullptr, nullptr, nullptr, O, dO, LSE, nullptr, nullptr, nullptr, workspace, B, H, n, d,
+                            1.0f, -1, 1),
+                 exattn::kStageRowdot, stream);
 }
 
 int attn_bwd_dkdv_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* Q, const void* K,
@@ -175,9 +191,10 @@ int attn_bwd_dkdv_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void
   const Span outs[] = {{dK, kb}, {dV, kb}};
   st = check_bwd(dtype, B, H, Hkv, n, d, scale, window, ins, 6, outs, 2, workspace_bytes);
   if (st != EXATTN_OK) return st;
-  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, nullptr, dK, dV, (float*)workspace,
-                      B, H, n, d, scale, window, H / Hkv};
-  return run_bwd(dtype, p, exattn::kStageKV, stream);
+  return run_bwd(dtype,
+                 bwd_params(Q, K, V, nullptr, dO, LSE, nullptr, dK, dV, workspace, B, H, n, d, scale, window,
+                            H / Hkv),
+                 exattn::kStageKV, stream);
 }
 
 int attn_bwd_dkdv(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
@@ -200,9 +217,10 @@ int attn_bwd_dq_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* 
   const Span outs[] = {{dQ, tb}};
   st = check_bwd(dtype, B, H, Hkv, n, d, scale, window, ins, 6, outs, 1, workspace_bytes);
   if (st != EXATTN_OK) return st;
-  exattn::BwdParams p{Q, K, V, nullptr, dO, LSE, dQ, nullptr, nullptr, (float*)workspace,
-                      B, H, n, d, scale, window, H / Hkv};
-  return run_bwd(dtype, p, exattn::kStageQ, stream);
+  return run_bwd(dtype,
+                 bwd_params(Q, K, V, nullptr, dO, LSE, dQ, nullptr, nullptr, workspace, B, H, n, d, scale, window,
+                            H / Hkv),
+                 exattn::kStageQ, stream);
 }
 
 int attn_bwd_dq(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,

@@ -38,7 +38,7 @@ struct KvCfg {
 template <int D, bool WINDOWED>
 __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-    const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
+    const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int n, int n_kblocks, int total_blocks, float scale,
     float scale_log2, int window, int group) {
   constexpr int NW = KvCfg<D>::NW;
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
 
   __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BQ * D];  // [buf][Q/dO]
   __shared__ __attribute__((aligned(16))) __bf16 vres[BKV * D];        // this block's V rows
-  __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE / D]
+  __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE*log2(e) / D]
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int kvh = bid / n_kblocks;  // key/value head (batch-major)
@@ -88,9 +88,10 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   if constexpr (WINDOWED) band_keys(my_key, my_key + 1, n, window, &row_lo, &row_hi);
   const unsigned row_span = (unsigned)max(row_hi - row_lo, 0);
 
-  // Q and dO tiles, and the LSE and D values of their rows, go straight from
-  // global memory to LDS.  Rows past n are clamped copies of row n-1; their
-  // probabilities are masked to zero on the tail tile.
+  // Q and dO tiles, and the LSE*log2(e) and D values of their rows, go
+  // straight from global memory to LDS.  Rows past n are clamped copies of
+  // row n-1 with LSE = +inf, so their probabilities (and dS) are exactly zero
+  // without a per-element test.
   using Tile = TileAsync<D, BQ, NT>;
   static_assert(BQ == 32, "the row-statistics copy maps 64 lanes to 2 x 32 rows");
   auto load_tile = [&](int t, int qg, int buf) {
@@ -99,9 +100,10 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
     const int qrow = (qh0 + qg) * n + i0;
     Tile::issue(Qg + qrow * D, n - i0, tiles[buf][0], tid);
     Tile::issue(dOg + qrow * D, n - i0, tiles[buf][1], tid);
-    if (wave == 0) {  // lanes 0-31: LSE of rows i0.., lanes 32-63: D
+    if (wave == 0) {  // lanes 0-31: LSE*log2(e) of rows i0.., lanes 32-63: D
       const int i = qrow + min(l32, n - 1 - i0);
-      lds_dma4(hi ? (const void*)(Dg + i) : (const void*)(LSEg + i), &rowst[buf][0][0]);
+      const void* src = hi ? (const void*)(Dg + i) : i0 + l32 < n ? (const void*)(LSE2g + i) : (const void*)&kPosInf;
+      lds_dma4(src, &rowst[buf][0][0]);
     }
   };
 
@@ -139,12 +141,12 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
       dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), lds_row_frag<D>(vres, wave * 32 + l32, ds, hi), dp);
     }
 
-    // Rows past n (tail tile) and, with a window, queries outside this
-    // lane's key band get P = 0.
-    bool need_mask = i0 + BQ > n;
+    // With a window, queries outside this lane's key band get P = 0 (rows
+    // past n already have P = 0 through their LSE).
+    bool need_mask = false;
     if constexpr (WINDOWED) {
       const int k_lo_w = kb0 + wave * 32;
-      need_mask = need_mask || max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
+      need_mask = max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -154,9 +156,9 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g + j;
-        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j] * kLog2e));
+        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j]));
         // queries that see this lane's key: [row_lo, row_lo + row_span)
-        if (need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
+        if (WINDOWED && need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
         s[r] = p;
         dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
       }
@@ -217,7 +219,7 @@ struct QCfg<256> {
 template <int D, bool WINDOWED>
 __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-    const __bf16* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
+    const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
     __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window,
     int group) {
   constexpr int NW = QCfg<D>::NW;
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
       qreg[ds] = __builtin_bit_cast(bf16x8, ok ? qs[2 * ds] : u32x4{0, 0, 0, 0});
       greg[ds] = __builtin_bit_cast(bf16x8, ok ? gs[2 * ds] : u32x4{0, 0, 0, 0});
     }
-    lse2 = ok ? LSEg[(size_t)head * n + my_row] * kLog2e : __builtin_huge_valf();
+    lse2 = ok ? LSE2g[(size_t)head * n + my_row] : __builtin_huge_valf();
     dl = ok ? Dg[(size_t)head * n + my_row] : 0.0f;
   }
 
@@ -266,12 +268,14 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
   if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
   const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
 
-  // K and V tiles go straight from global memory to LDS; key rows past n are
-  // clamped copies whose probabilities are masked to zero.
+  // K and V tiles go straight from global memory to LDS.  Key rows past n
+  // are zeros in the K tile, so whatever their dS, they add exactly nothing
+  // to dQ = dS K (their V rows are clamped copies and only feed that dS).
   using Tile = TileAsync<D, BC, NT>;
+  using TileK = TileAsyncZeroTail<D, BC, NT>;
   auto load_tile = [&](int t, int buf) {
     const int kbase = t * BC;
-    Tile::issue(K + (size_t)kbase * D, n - kbase, tiles[buf][0], tid);
+    TileK::issue(K + (size_t)kbase * D, n - kbase, tiles[buf][0], tid);
     Tile::issue(V + (size_t)kbase * D, n - kbase, tiles[buf][1], tid);
   };
 
@@ -303,17 +307,19 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
       }
     }
 
-    bool need_mask = kbase + BC > n;
+    // With a window, keys outside this lane's row band get P = 0 (keys past
+    // n meet zero K rows).
+    bool need_mask = false;
     if constexpr (WINDOWED) {
       const int r_lo = q0 + wave * 32;
-      need_mask = need_mask || max(r_lo + 31 - kbase, kbase + BC - 1 - r_lo) > window;
+      need_mask = max(r_lo + 31 - kbase, kbase + BC - 1 - r_lo) > window;
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
-        if (need_mask) {
+        if (WINDOWED && need_mask) {
           const int key = kbase + kb * 32 + acc_row(r, lane);
           p = (unsigned)(key - key_lo) < key_span ? p : 0.0f;
         }
@@ -360,12 +366,13 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   if (tk > 0x7fffffffL || tq > 0x7fffffffL) return hipErrorInvalidValue;
 
   if (stages & kStageRowdot) {
-    hipError_t e = launch_rowdot<__bf16>((const __bf16*)p.o, (const __bf16*)p.dout, p.delta, heads * p.n, D, stream);
+    hipError_t e = launch_rowdot<__bf16>((const __bf16*)p.o, (const __bf16*)p.dout, p.lse, p.delta, p.lse2,
+                                         heads * p.n, D, stream);
     if (e != hipSuccess) return e;
   }
   if (stages & kStageKV) {
     hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(KvCfg<D>::NW * 64), 0, stream,
-                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
+                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
                        p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window,
                        p.group);
     hipError_t e = hipGetLastError();
@@ -373,7 +380,7 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   }
   if (stages & kStageQ) {
     hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(QCfg<D>::NW * 64), 0, stream,
-                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse,
+                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
                        p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

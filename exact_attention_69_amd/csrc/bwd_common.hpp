@@ -6,12 +6,14 @@
 namespace exattn {
 
 // D_i = sum_k dO_ik * O_ik in fp32 (the row term of dS = P * (dP - D) that
-// the chain rule of the softmax produces).  Each thread reduces 8 contiguous
-// elements; the D/8 threads of a row combine their partial sums with xor
-// shuffles.  rows = B*H*n.
+// the chain rule of the softmax produces), and LSE_i * log2(e), the base-2
+// form of the log-sum-exp that the gradient kernels subtract from their
+// base-2 scores.  Each thread reduces 8 contiguous elements; the D/8 threads
+// of a row combine their partial sums with xor shuffles.  rows = B*H*n.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                         float* __restrict__ delta, long rows) {
+                                                         const float* __restrict__ lse, float* __restrict__ delta,
+                                                         float* __restrict__ lse2, long rows) {
   constexpr int TPR = D / 8;  // threads per row
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = gid / TPR;
@@ -25,17 +27,29 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ O
   }
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 template <typename T>
-hipError_t launch_rowdot(const T* O, const T* dO, float* delta, long rows, int d, hipStream_t stream) {
+hipError_t launch_rowdot(const T* O, const T* dO, const float* lse, float* delta, float* lse2, long rows, int d,
+                         hipStream_t stream) {
   const long threads = rows * (d / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   switch (d) {
-    case 64: hipLaunchKernelGGL((bwd_rowdot_kernel<T, 64>), dim3(blocks), dim3(256), 0, stream, O, dO, delta, rows); break;
-    case 128: hipLaunchKernelGGL((bwd_rowdot_kernel<T, 128>), dim3(blocks), dim3(256), 0, stream, O, dO, delta, rows); break;
-    case 256: hipLaunchKernelGGL((bwd_rowdot_kernel<T, 256>), dim3(blocks), dim3(256), 0, stream, O, dO, delta, rows); break;
+    case 64:
+      hipLaunchKernelGGL((bwd_rowdot_kernel<T, 64>), dim3(blocks), dim3(256), 0, stream, O, dO, lse, delta, lse2, rows);
+      break;
+    case 128:
+      hipLaunchKernelGGL((bwd_rowdot_kernel<T, 128>), dim3(blocks), dim3(256), 0, stream, O, dO, lse, delta, lse2,
+                         rows);
+      break;
+    case 256:
+      hipLaunchKernelGGL((bwd_rowdot_kernel<T, 256>), dim3(blocks), dim3(256), 0, stream, O, dO, lse, delta, lse2,
+                         rows);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

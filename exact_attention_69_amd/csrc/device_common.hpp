@@ -179,6 +179,33 @@ struct TileAsync {
   }
 };
 
+// Constant sources for the direct copies of tile rows past the end of the
+// sequence: a row of zeros (any head dim up to 256) and +infinity.
+__device__ const __bf16 kZeroRow[256] = {};
+__device__ const float kPosInf = __builtin_huge_valf();
+
+// As TileAsync, but rows at or beyond `valid` are copied from kZeroRow, so
+// they hold exact zeros in LDS.
+template <int D, int ROWS, int NT>
+struct TileAsyncZeroTail {
+  static_assert(D <= 256, "kZeroRow holds 256 elements");
+  static constexpr int CPR = D / 8;
+  static constexpr int IT = ROWS * CPR / NT;
+  static_assert((ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
+  static __device__ __forceinline__ void issue(const __bf16* __restrict__ src, int valid, __bf16* lds, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int slot0 = it * NT + wave * 64;
+      const int p = slot0 + lane;
+      const int row = p / CPR;
+      const int c = swz_chunk<D>(row, p % CPR);
+      lds_dma16(row < valid ? (const void*)(src + (size_t)row * D + 8 * c) : (const void*)(kZeroRow + 8 * c),
+                lds + 8 * slot0);
+    }
+  }
+};
+
 // Wait for every outstanding memory operation of this wave (including direct
 // global -> LDS copies), then synchronise the workgroup.
 __device__ __forceinline__ void wait_all_and_barrier() {

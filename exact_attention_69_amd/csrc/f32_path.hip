@@ -283,8 +283,8 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const long total_kv = total / p.group;  // key blocks: one set per key/value head
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
   if (stages & kStageRowdot) {
-    hipError_t e = launch_rowdot<float>((const float*)p.o, (const float*)p.dout, p.delta, (long)p.B * p.H * p.n, D,
-                                        stream);
+    hipError_t e = launch_rowdot<float>((const float*)p.o, (const float*)p.dout, p.lse, p.delta, p.lse2,
+                                        (long)p.B * p.H * p.n, D, stream);
     if (e != hipSuccess) return e;
   }
   if (stages & kStageKV) {

@@ -29,6 +29,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;  // workspace: [B, H, n] fp32, D = rowsum(dO * O)
+  float* lse2;   // workspace: [B, H, n] fp32, LSE * log2(e)
   int B, H, n, d;
   float scale;
   int window;

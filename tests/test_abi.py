@@ -110,8 +110,10 @@ def test_forward_rejects_null_misaligned_and_overlapping(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.attn_bwd_workspace_bytes(1, 2, 32, 8192, 128) >= 2 * 32 * 8192 * 4
-    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 64) >= 256 * 4
+    # two fp32 row arrays (D and LSE*log2e), each 256-byte aligned
+    assert lib.attn_bwd_workspace_bytes(1, 2, 32, 8192, 128) == 2 * (2 * 32 * 8192 * 4)
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 64) == 2 * 256 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 1, 1, 100, 64) == 2 * 512
     assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 48) == 0
     assert lib.attn_bwd_workspace_bytes(1, 0, 1, 256, 64) == 0
 
@@ -137,10 +139,12 @@ def test_backward_rejects_bad_arguments(lib):
 def test_backward_stages_reject_bad_arguments(lib):
     need = lib.attn_bwd_workspace_bytes(1, 1, 1, 128, 64)
     q, k, v, do, lse, dk, dv, ws = ptrs(8)
-    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, ws, need - 1, None) == EWORKSPACE
-    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, None, ws, need, None) == EINVAL
-    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, q, need, None) == EINVAL  # workspace aliases O
-    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 72, q, do, ws, need, None) == EUNSUPPORTED
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, lse, ws, need - 1, None) == EWORKSPACE
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, None, lse, ws, need, None) == EINVAL
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, None, ws, need, None) == EINVAL
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, lse, q, need, None) == EINVAL  # workspace aliases O
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 64, q, do, lse, lse, need, None) == EINVAL  # workspace aliases LSE
+    assert lib.attn_bwd_rowdot(1, 1, 1, 128, 72, q, do, lse, ws, need, None) == EUNSUPPORTED
     assert lib.attn_bwd_dkdv(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, dk, dv, ws, need - 1, None) == EWORKSPACE
     assert lib.attn_bwd_dkdv(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -1, dk, dk, ws, need, None) == EINVAL
     assert lib.attn_bwd_dkdv(1, 1, 1, 128, 64, q, k, v, do, lse, 0.1, -3, dk, dv, ws, need, None) == EINVAL

@@ -97,7 +97,7 @@ def test_gqa_staged_backward_matches_one_call(dtype, window):
     t = to_device(draw_inputs(wl), dtype)
     o, lse = ea.attn_fwd_gqa(t["q"], t["k"], t["v"], window=window)
     ref = ea.attn_bwd_gqa(t["q"], t["k"], t["v"], o, t["do"], lse, window=window)
-    ws = ea.attn_bwd_rowdot(o, t["do"])
+    ws = ea.attn_bwd_rowdot(o, t["do"], lse)
     dk, dv = ea.attn_bwd_dkdv_gqa(t["q"], t["k"], t["v"], t["do"], lse, ws, window=window)
     dq = ea.attn_bwd_dq_gqa(t["q"], t["k"], t["v"], t["do"], lse, ws, window=window)
     torch.cuda.synchronize()

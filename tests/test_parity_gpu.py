@@ -157,7 +157,7 @@ def test_staged_backward_matches_attn_bwd(dtype, window):
     t = to_device(draw_inputs(wl), dtype)
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], window=window)
     ref = ea.attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, window=window)
-    ws = ea.attn_bwd_rowdot(o, t["do"])
+    ws = ea.attn_bwd_rowdot(o, t["do"], lse)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     dk, dv = ea.attn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], lse, ws, window=window)
