@@ -128,19 +128,20 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
 
   // S^T for one K tile in LDS: lanes = query rows, registers = keys.  Each K
   // fragment feeds the RB row blocks.
+  // S^T of key block kb of one K tile in LDS.
+  auto compute_s_block = [&](const __bf16* Ks, int kb, f32x16 (&s)[RB][NKB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s[rb][kb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const bf16x8 a = lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma32(a, qreg[rb][ds], s[rb][kb]);
+    }
+  };
   auto compute_s = [&](const __bf16* Ks, f32x16 (&s)[RB][NKB]) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[rb][kb] = f32x16{};
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma32(a, qreg[rb][ds], s[rb][kb]);
-      }
+    for (int kb = 0; kb < NKB; ++kb) compute_s_block(Ks, kb, s);
   };
 
   f32x16 o[RB][NDB];
@@ -217,41 +218,35 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
       msub[rb] = m_run[rb] == kNegInf ? 0.0f : m_run[rb];
     }
 
-    // ---- S for the next tile (matrix cores) || exponentials (vector ALU) ----
-    // On the last tile this reads a stale K buffer; the result is unused.
-    f32x16 s_nxt[RB][NKB];
-    compute_s(kbuf[(j + 1) & 1], s_nxt);
-    // P in bf16 (the operand of the P V product); the fp32 row sum is split
-    // over independent partial sums to keep the add chain short.
+    // ---- exponentials (vector ALU) || S of the next tile (matrix cores) -----
+    // P of key block kb goes to bf16 (the operand of the P V product); once a
+    // block is converted its fp32 registers receive that block of the next
+    // tile's S, so the next S needs no registers of its own and the
+    // exponentials of block kb+1 run beside the matrix products of block kb.
+    // On the last tile the next S reads a stale K buffer; it is unused.  The
+    // fp32 row sum is split over independent partial sums.
     bf16x8 pb[RB][BC / 16];
+    float lsum[RB][4];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int i = 0; i < 4; ++i) lsum[rb][i] = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s_cur[rb][kb][r] = fast_exp2(__builtin_fmaf(s_cur[rb][kb][r], scale_log2, -msub[rb]));
-          lsum[r & 3] += s_cur[rb][kb][r];
+          lsum[rb][r & 3] += s_cur[rb][kb][r];
         }
         pb[rb][2 * kb] = acc_to_operand(s_cur[rb][kb], 0);
         pb[rb][2 * kb + 1] = acc_to_operand(s_cur[rb][kb], 1);
       }
-      l_part[rb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+      compute_s_block(kbuf[(j + 1) & 1], kb, s_cur);
     }
-    // Issue order: LDS reads run kLead reads ahead so their latency hides
-    // behind earlier MFMAs; the exponentials fill the gaps.
-    {
-      constexpr int NS = NKB * NDS, kLead = 4;
-      constexpr int VPER = RB * (4 * 16 * NKB + 8 * NKB) / NS + 1;
-      EXATTN_SCHED(kSchedDSRead, kLead);
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        EXATTN_SCHED(kSchedMFMA, RB);
-        if (i + kLead < NS) EXATTN_SCHED(kSchedDSRead, 1);
-        EXATTN_SCHED(kSchedVALU, VPER);
-      }
-    }
+    for (int rb = 0; rb < RB; ++rb) l_part[rb] += (lsum[rb][0] + lsum[rb][1]) + (lsum[rb][2] + lsum[rb][3]);
 
     // ---- O^T += V^T P^T -------------------------------------------------------
     // A operand (V^T): lane l needs V[key(t)][db*32 + l%32] with the keys in
@@ -276,10 +271,6 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     }
 
     wait_all_and_barrier();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s_cur[rb][kb] = s_nxt[rb][kb];
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -----------------------
