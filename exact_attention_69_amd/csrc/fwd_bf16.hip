@@ -49,7 +49,7 @@ struct FwdCfg<64> {
 };
 template <>
 struct FwdCfg<128> {
-  static constexpr int NW = 4, RB = 1, BC = 64, WPE = 2;
+  static constexpr int NW = 8, RB = 1, BC = 64, WPE = 2;  // 256 rows: one K/V tile copy per 8 waves
 };
 template <>
 struct FwdCfg<256> {
