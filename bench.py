@@ -59,21 +59,16 @@ def measured_traffic(wl, kernel):
     (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size), or None
     when the summary is for another workload or the kernel sources changed
     since the counters were taken."""
-    import glob
-    import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters_n8192_d128.md")
+    from exact_attention_69_amd.profsum import kernel_source_sha256
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_counters_{wl.name}.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
         return None
     info = json.loads(m.group(1))
-    h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "exact_attention_69_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
-    if info.get("workload") != wl.name or info.get("source_sha256") != h.hexdigest():
+    if info.get("workload") != wl.name or info.get("source_sha256") != kernel_source_sha256():
         return None
     k = info["kernels"].get(kernel)
     return None if k is None else int(k["hbm_bytes_per_launch"])

@@ -2,15 +2,37 @@
 
 usage: python -m exact_attention_69_amd.profsum stats <run_kernel_stats.csv> "<command>"
        python -m exact_attention_69_amd.profsum pmc <dir with p*/run_counter_collection.csv> "<command>"
+       python -m exact_attention_69_amd.profsum traffic <dir> <workload> <copy MiB> "<commands>"
+
+`traffic` reads <dir>/kt/run_kernel_stats.csv (a --kernel-trace --stats run)
+and <dir>/p*/run_counter_collection.csv (counter passes over the same
+program, which also ran one plain device copy of <copy MiB> MiB), scales
+FETCH_SIZE / WRITE_SIZE by what they read for that copy, and writes the
+per-kernel table plus a JSON block that bench.py reads for the roofline's
+`traffic` while the kernel sources still hash to the recorded value.
 """
 import collections
 import csv
 import glob
+import hashlib
+import json
+import os
 import re
 import sys
 
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def kernel_source_sha256():
+    """SHA-256 over the kernel sources (names and contents, sorted by name)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
 KERNEL_RE = re.compile(r"(fwd_bf16_kernel|bwd_kv_bf16_kernel|bwd_q_bf16_kernel|bwd_rowdot_kernel|fwd_f32_kernel|"
-                       r"bwd_kv_f32_kernel|bwd_q_f32_kernel|elementwise_kernel|copy\w*)(?:I[A-Za-z]*Li(\d+))?")
+                       r"bwd_kv_f32_kernel|bwd_q_f32_kernel|elementwise_kernel|copy\w*)(?:I\w*?Li(\d+))?")
 
 
 def short(name):
@@ -47,6 +69,81 @@ def pmc(directory, cmd):
     return "\n".join(out)
 
 
+def _counters(directory):
+    res = collections.defaultdict(lambda: collections.defaultdict(dict))
+    for path in sorted(glob.glob(directory + "/p*/run_counter_collection.csv")):
+        for row in csv.DictReader(open(path)):
+            d = res[short(row["Kernel_Name"])][row["Counter_Name"]]
+            d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in res.items()}
+
+
+def algorithmic_bytes(wl, kernel):
+    """(read, write) bytes a kernel must move at least, per launch."""
+    eb = 2 if wl.dtype == "bf16" else 4
+    t = wl.B * wl.H * wl.n * wl.d * eb
+    tkv = wl.B * wl.Hkv * wl.n * wl.d * eb
+    r = wl.B * wl.H * wl.n * 4
+    if kernel.startswith("fwd"):
+        return t + 2 * tkv, t + r                      # Q, K, V -> O, LSE
+    if kernel.startswith("bwd_rowdot"):
+        return 2 * t + r, 2 * r                        # O, dO, LSE -> D, LSE*log2e
+    if kernel.startswith("bwd_kv"):
+        return 2 * t + 2 * tkv + 2 * r, 2 * tkv        # Q, dO, K, V, LSE*log2e, D -> dK, dV
+    if kernel.startswith("bwd_q"):
+        return 2 * t + 2 * tkv + 2 * r, t              # Q, dO, K, V, LSE*log2e, D -> dQ
+    return None
+
+
+def traffic(directory, workload_name, copy_mib, cmds):
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from workloads import workload
+    wl = workload(workload_name)
+    kt = {short(r["Name"]): r for r in csv.DictReader(open(os.path.join(directory, "kt", "run_kernel_stats.csv")))}
+    cnt = _counters(directory)
+    copy = [k for k in cnt if "copy" in k.lower()]
+    if not copy:
+        raise SystemExit("no copy kernel in the counter passes (run them with --copy-calibration)")
+    c = cnt[copy[0]]
+    copy_kib = copy_mib * 1024.0
+    fs, ws = copy_kib / c["FETCH_SIZE"], copy_kib / c["WRITE_SIZE"]
+    out = [f"# HBM traffic and counters: one bench step of {wl.name}, MI355X", "",
+           "Commands (one counter set per run; each counter run also performs one plain device copy of "
+           f"{copy_mib} MiB, whose counters calibrate the HBM figures):", "", "```"] + cmds + ["```", "",
+           f"Calibration ({copy[0]} moving {copy_mib} MiB = {copy_kib:.0f} KiB): FETCH_SIZE read "
+           f"{c['FETCH_SIZE']:.0f} KiB -> fetch scale {fs:.4f}; WRITE_SIZE read {c['WRITE_SIZE']:.0f} KiB -> "
+           f"write scale {ws:.4f}.", "",
+           "| kernel | avg ms (trace) | HBM read MiB (scaled) | HBM write MiB (scaled) | algorithmic read / write "
+           "MiB | HBM GB/s | MFMA busy % | clock GHz | LDS bank conflicts | MFMA TFLOP executed |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    js = {"workload": wl.name, "fetch_scale": round(fs, 6), "write_scale": round(ws, 6),
+          "source_sha256": kernel_source_sha256(), "kernels": {}}
+    for k, cs in cnt.items():
+        if k in copy or "FETCH_SIZE" not in cs or k not in kt:
+            continue
+        ms = float(kt[k]["AverageNs"]) / 1e6
+        rd, wr = cs["FETCH_SIZE"] * fs * 1024, cs["WRITE_SIZE"] * ws * 1024
+        alg = algorithmic_bytes(wl, k)
+        gui = cs.get("GRBM_GUI_ACTIVE", 0.0) / 8  # per-XCD cycles
+        busy = 100.0 * cs.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * gui) if gui else 0.0
+        clock = gui / (ms * 1e6) if ms else 0.0
+        mops = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / 1e12
+        algs = f"{alg[0] / 2**20:.0f} / {alg[1] / 2**20:.0f}" if alg else "-"
+        out.append(f"| {k} | {ms:.3f} | {rd / 2**20:.0f} | {wr / 2**20:.0f} | {algs} | {(rd + wr) / (ms * 1e6):.0f} | "
+                   f"{busy:.1f} | {clock:.2f} | {cs.get('SQ_LDS_BANK_CONFLICT', 0.0):.0f} | {mops:.3f} |")
+        js["kernels"][k] = {"avg_ms_trace": round(ms, 4), "fetch_kib": round(cs["FETCH_SIZE"], 1),
+                            "write_kib": round(cs["WRITE_SIZE"], 1), "hbm_bytes_per_launch": int(rd + wr)}
+    out += ["", "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE/8 XCDs); clock = "
+            "(GRBM_GUI_ACTIVE/8) / trace duration; executed MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", "",
+            "Machine-readable (read by bench.py; valid only while the kernel sources hash to `source_sha256`):",
+            "", "```json", json.dumps(js, indent=1), "```"]
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    mode, path, cmd = sys.argv[1], sys.argv[2], sys.argv[3]
-    print(stats(path, cmd) if mode == "stats" else pmc(path, cmd))
+    mode = sys.argv[1]
+    if mode == "traffic":
+        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5].split("\n")))
+    else:
+        path, cmd = sys.argv[2], sys.argv[3]
+        print(stats(path, cmd) if mode == "stats" else pmc(path, cmd))
