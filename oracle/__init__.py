@@ -24,3 +24,8 @@ from .attention import (  # noqa: F401
     forward_rows,
     backward_dq_rows,
 )
+from .pattern import (  # noqa: F401
+    Pattern,
+    attention_forward_pattern,
+    attention_backward_pattern,
+)
