@@ -37,10 +37,23 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 
-def flops(wl):
-    from workloads import pair_count
-    pairs = pair_count(wl.n, wl.window) * wl.B * wl.H
-    return 4.0 * pairs * wl.d, 10.0 * pairs * wl.d
+_PAIRS = {}
+
+
+def flops(wl, pairs=False):
+    """Algorithmic (fwd, bwd) FLOPs: 4 and 10 x visible pairs x d, over all
+    heads; with pairs=True, the visible (query, key) pairs of one head."""
+    from workloads import draw_pattern, pair_count, pattern_pair_count
+    if wl.name not in _PAIRS:
+        if wl.has_pattern:
+            window, glob, layout = draw_pattern(wl)
+            _PAIRS[wl.name] = pattern_pair_count(wl.n, window, glob, layout)
+        else:
+            _PAIRS[wl.name] = pair_count(wl.n, wl.window)
+    if pairs:
+        return _PAIRS[wl.name]
+    p = _PAIRS[wl.name] * wl.B * wl.H
+    return 4.0 * p * wl.d, 10.0 * p * wl.d
 
 
 def hbm_bytes(wl):
@@ -112,11 +125,15 @@ def kernel_names(wl):
 
 def time_steps(wl, steps, warmup):
     """Run `warmup` untimed and `steps` timed steps of the workload with its
-    inputs resident on the GPU; returns (per-kernel average ms [fwd, rowdot,
-    dK/dV, dQ], ms per step, wall seconds of the timed region)."""
+    inputs resident on the GPU; returns (names and average ms of the calls of
+    a step, ms per step, wall seconds of the timed region).  Dense workloads
+    time the four kernels of a step (forward, rowdot, dK/dV, dQ) one call
+    each; sparse-pattern workloads time attn_fwd_pattern and attn_bwd_pattern
+    (each including its plan kernels)."""
+    import numpy as np
     import torch
     import exact_attention_69_amd as ea
-    from workloads import draw_inputs
+    from workloads import draw_inputs, draw_pattern
 
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -128,27 +145,38 @@ def time_steps(wl, steps, warmup):
     lse = torch.empty((wl.B, wl.H, wl.n), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     code = ea.EXATTN_BF16 if wl.dtype == "bf16" else ea.EXATTN_F32
-    ws = torch.empty(max(ea.attn_bwd_workspace_bytes(code, wl.B, wl.H, wl.n, wl.d), 256), dtype=torch.uint8,
-                     device=dev)
     stream = torch.cuda.current_stream(dev)
-    gqa = wl.Hkv != wl.H
-    attn_fwd = ea.attn_fwd_gqa if gqa else ea.attn_fwd
-    attn_bwd_dkdv = ea.attn_bwd_dkdv_gqa if gqa else ea.attn_bwd_dkdv
-    attn_bwd_dq = ea.attn_bwd_dq_gqa if gqa else ea.attn_bwd_dq
-
-    # The backward runs as its three stage calls (the same three kernels that
-    # attn_bwd launches), so that every kernel is bracketed by its own events.
-    calls = (lambda: attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream),
-             lambda: ea.attn_bwd_rowdot(o, do, lse, workspace=ws, stream=stream),
-             lambda: attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=stream),
-             lambda: attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=stream))
+    if wl.has_pattern:
+        window, glob, layout = draw_pattern(wl)
+        pat = ea.AttnPattern(window, torch.from_numpy(glob).to(dev) if len(glob) else None,
+                             torch.from_numpy(layout).to(dev) if layout is not None else None)
+        ws = torch.empty(ea.attn_pattern_workspace_bytes(code, wl.B, wl.H, wl.n, wl.d), dtype=torch.uint8,
+                         device=dev)
+        names = ["attn_fwd_pattern", "attn_bwd_pattern"]
+        calls = (lambda: ea.attn_fwd_pattern(q, k, v, pat, wl.scale, out=o, lse=lse, workspace=ws, stream=stream),
+                 lambda: ea.attn_bwd_pattern(q, k, v, o, do, lse, pat, wl.scale, workspace=ws, dq=dq, dk=dk, dv=dv,
+                                             stream=stream))
+    else:
+        ws = torch.empty(max(ea.attn_bwd_workspace_bytes(code, wl.B, wl.H, wl.n, wl.d), 256), dtype=torch.uint8,
+                         device=dev)
+        gqa = wl.Hkv != wl.H
+        attn_fwd = ea.attn_fwd_gqa if gqa else ea.attn_fwd
+        attn_bwd_dkdv = ea.attn_bwd_dkdv_gqa if gqa else ea.attn_bwd_dkdv
+        attn_bwd_dq = ea.attn_bwd_dq_gqa if gqa else ea.attn_bwd_dq
+        names = kernel_names(wl)
+        # The backward runs as its three stage calls (the same three kernels
+        # that attn_bwd launches), so that every kernel has its own events.
+        calls = (lambda: attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream),
+                 lambda: ea.attn_bwd_rowdot(o, do, lse, workspace=ws, stream=stream),
+                 lambda: attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=stream),
+                 lambda: attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=stream))
     for _ in range(warmup):
         for c in calls:
             c()
     torch.cuda.synchronize()
 
     # Whole steps, bracketed by device syncs, timed with events on the stream
-    # the kernels are launched on; one event between consecutive kernels.
+    # the kernels are launched on; one event between consecutive calls.
     nk = len(calls)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -164,7 +192,7 @@ def time_steps(wl, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     kms = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(nk)]
-    return kms, start.elapsed_time(end) / steps, wall
+    return names, kms, start.elapsed_time(end) / steps, wall
 
 
 def main(argv=None):
@@ -188,7 +216,7 @@ def main(argv=None):
 
     wl = workload(args.workload)
     fwd_f, bwd_f = flops(wl)
-    kms, ms, wall = time_steps(wl, args.steps, args.warmup)
+    names, kms, ms, wall = time_steps(wl, args.steps, args.warmup)
     nk = len(kms)
     fwd_ms = kms[0]
     bwd_ms = sum(kms[1:])
@@ -200,8 +228,9 @@ def main(argv=None):
     #   dK/dV pass    8*B*H*pairs*d  (S, dP = dO V^T, dV = P^T dO, dK = dS^T Q)
     #   dQ pass       6*B*H*pairs*d  (S, dP, dQ = dS K)
     #   rowdot        memory bound (reads O, dO and LSE, writes D and LSE*log2e)
-    kernel_flops = [fwd_f, None, 0.8 * bwd_f, 0.6 * bwd_f]
-    names = kernel_names(wl)
+    #   (sparse patterns: one forward call and one backward call, each with
+    #   its plan kernels)
+    kernel_flops = [fwd_f, bwd_f] if wl.has_pattern else [fwd_f, None, 0.8 * bwd_f, 0.6 * bwd_f]
     dom = max(range(nk), key=lambda i: kms[i])
     ach = kernel_flops[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
@@ -212,16 +241,20 @@ def main(argv=None):
     variants = {}
     if not args.no_variants:
         for vw in VARIANTS:
-            vk, vms, _ = time_steps(vw, args.variant_steps, 3)
+            vn, vk, vms, _ = time_steps(vw, args.variant_steps, 3)
             vf, vb = flops(vw)
-            vn = kernel_names(vw)
-            variants[vw.name] = {
-                "value": round((vf + vb) / (vms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(vms, 4),
-                "steps": args.variant_steps, "B": vw.B, "H": vw.H, "Hkv": vw.Hkv, "n": vw.n, "d": vw.d,
-                "window": vw.window, "kernel_ms": {vn[i]: round(vk[i], 4) for i in range(nk)},
-                "kernel_tflops": {vn[i]: round(f / (vk[i] * 1e-3) / 1e12, 2)
-                                  for i, f in enumerate([vf, None, 0.8 * vb, 0.6 * vb]) if f},
-                "hbm_gbs_algorithmic": round(sum(hbm_bytes(vw)) / (vms * 1e-3) / 1e9, 1)}
+            entry = {"value": round((vf + vb) / (vms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                     "ms_per_step": round(vms, 4), "steps": args.variant_steps, "B": vw.B, "H": vw.H, "Hkv": vw.Hkv,
+                     "n": vw.n, "d": vw.d, "window": vw.window, "kernel_ms": {vn[i]: round(vk[i], 4) for i in range(len(vn))}}
+            if vw.has_pattern:
+                entry.update(n_global=vw.n_global, bigbird=list(vw.bigbird), visible_pairs_per_head=flops(vw, pairs=True),
+                             fwd_tflops=round(vf / (vk[0] * 1e-3) / 1e12, 2),
+                             bwd_tflops=round(vb / (vk[1] * 1e-3) / 1e12, 2))
+            else:
+                entry["kernel_tflops"] = {vn[i]: round(f / (vk[i] * 1e-3) / 1e12, 2)
+                                          for i, f in enumerate([vf, None, 0.8 * vb, 0.6 * vb]) if f}
+            entry["hbm_gbs_algorithmic"] = round(sum(hbm_bytes(vw)) / (vms * 1e-3) / 1e9, 1)
+            variants[vw.name] = entry
 
     if args.copy_calibration:
         import torch

@@ -7,6 +7,7 @@ include/exattn.h); this package only marshals PyTorch device tensors into it.
 from ._binding import (  # noqa: F401
     EXATTN_BF16,
     EXATTN_F32,
+    AttnPattern,
     ExattnError,
     LIB_PATH,
     attn_bwd,
@@ -15,10 +16,13 @@ from ._binding import (  # noqa: F401
     attn_bwd_dq,
     attn_bwd_dq_gqa,
     attn_bwd_gqa,
+    attn_bwd_pattern,
     attn_bwd_rowdot,
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_fwd_gqa,
+    attn_fwd_pattern,
+    attn_pattern_workspace_bytes,
     exattn_status_string,
     load_library,
 )

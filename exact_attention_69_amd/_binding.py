@@ -21,6 +21,37 @@ STATUS = {0: "EXATTN_OK", -1: "EXATTN_EINVAL", -2: "EXATTN_EUNSUPPORTED", -3: "E
 _lib = None
 
 
+class ExattnPatternC(ctypes.Structure):
+    """The C ABI's exattn_pattern descriptor (device pointers inside)."""
+    _fields_ = [("window", ctypes.c_int), ("n_global", ctypes.c_int), ("global_idx", ctypes.c_void_p),
+                ("layout_block", ctypes.c_int), ("layout", ctypes.c_void_p)]
+
+
+class AttnPattern:
+    """Sparse pattern on the GPU: window (-1: none), global token positions
+    (int32 tensor or None) and a 64-token block layout (uint8 [nb, nb] tensor
+    or None).  Holds references to the tensors while in use."""
+
+    def __init__(self, window=-1, global_idx=None, layout=None):
+        self.window = int(window)
+        self.global_idx = global_idx
+        self.layout = layout
+
+    def as_c(self, n, device):
+        torch = _torch()
+        g, lay = self.global_idx, self.layout
+        if g is not None:
+            if g.dtype != torch.int32 or g.dim() != 1 or not g.is_contiguous() or g.device != device:
+                raise ValueError("global_idx must be a contiguous int32 1-D tensor on the inputs' device")
+        if lay is not None:
+            nb = -(-n // 64)
+            if lay.dtype != torch.uint8 or tuple(lay.shape) != (nb, nb) or not lay.is_contiguous() \
+                    or lay.device != device:
+                raise ValueError(f"layout must be a contiguous uint8 [{nb}, {nb}] tensor on the inputs' device")
+        return ExattnPatternC(self.window, 0 if g is None else g.numel(), None if g is None else g.data_ptr(),
+                              0 if lay is None else 64, None if lay is None else lay.data_ptr())
+
+
 class ExattnError(RuntimeError):
     def __init__(self, fn, status, msg):
         super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
@@ -59,6 +90,13 @@ def load_library(path=None):
     lib.attn_bwd_dkdv_gqa.restype = ci
     lib.attn_bwd_dq_gqa.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, cs, vp]
     lib.attn_bwd_dq_gqa.restype = ci
+    lib.attn_pattern_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.attn_pattern_workspace_bytes.restype = cs
+    pp = ctypes.POINTER(ExattnPatternC)
+    lib.attn_fwd_pattern.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, cf, pp, vp, vp, vp, cs, vp]
+    lib.attn_fwd_pattern.restype = ci
+    lib.attn_bwd_pattern.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, pp, vp, vp, vp, vp, cs, vp]
+    lib.attn_bwd_pattern.restype = ci
     lib.exattn_status_string.argtypes = [ci]
     lib.exattn_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -302,3 +340,55 @@ def attn_bwd_dq_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None,
           do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), workspace.data_ptr(),
           workspace.numel() * workspace.element_size(), (q.device, _stream_ptr(q, stream)))
     return dq
+
+
+# ---------------------------------------------------------------------------
+# Sparse patterns: window + global tokens + block layout
+# ---------------------------------------------------------------------------
+
+def attn_pattern_workspace_bytes(dtype_code, B, H, n, d):
+    return int(load_library().attn_pattern_workspace_bytes(dtype_code, B, H, n, d))
+
+
+def _pattern_workspace(q, workspace):
+    torch = _torch()
+    B, H, n, d = q.shape
+    need = attn_pattern_workspace_bytes(_dtype_code(q), B, H, n, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def attn_fwd_pattern(q, k, v, pattern, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Forward over a sparse pattern (AttnPattern).  Returns (O, LSE)."""
+    torch = _torch()
+    _check_inputs(q, k, v)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    workspace, wsb = _pattern_workspace(q, workspace)
+    pc = pattern.as_c(n, q.device)
+    _call("attn_fwd_pattern", _dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale,
+          ctypes.byref(pc), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), wsb,
+          (q.device, _stream_ptr(q, stream)))
+    return out, lse
+
+
+def attn_bwd_pattern(q, k, v, o, do, lse, pattern, scale=None, workspace=None, dq=None, dk=None, dv=None,
+                     stream=None):
+    """Backward over a sparse pattern (AttnPattern).  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    _check_inputs(q, k, v, o, do)
+    _check_lse(lse, q)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    workspace, wsb = _pattern_workspace(q, workspace)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    pc = pattern.as_c(n, q.device)
+    _call("attn_bwd_pattern", _dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), scale, ctypes.byref(pc), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+          workspace.data_ptr(), wsb, (q.device, _stream_ptr(q, stream)))
+    return dq, dk, dv

@@ -231,3 +231,175 @@ int attn_bwd_dq(int dtype, int B, int H, int n, int d, const void* Q, const void
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Sparse patterns (window + global tokens + block layout)
+// ---------------------------------------------------------------------------
+namespace {
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace layout for a pattern problem: [global bitmap][forward lists]
+// [key-side lists][query-side lists][D][LSE*log2(e)], each region 256-byte
+// aligned.  Lists hold, per workgroup row of the kernel's grid, one entry per
+// tile of the other side (the most a workgroup can visit) and a count.
+struct PatternLayout {
+  size_t bitmap, fwd, kv, q, rows, total;
+  int fwd_R, fwd_T, fwd_NW, kv_R, kv_T, kv_NW, q_R, q_T, q_NW;
+  int fwd_blocks, fwd_tiles, kv_blocks, kv_tiles, q_blocks, q_tiles;
+};
+
+PatternLayout pattern_layout(int B, int H, int n, int d) {
+  PatternLayout L{};
+  exattn::fwd_bf16_geometry(d, &L.fwd_R, &L.fwd_T, &L.fwd_NW);
+  exattn::bwd_kv_bf16_geometry(d, &L.kv_R, &L.kv_T, &L.kv_NW);
+  exattn::bwd_q_bf16_geometry(d, &L.q_R, &L.q_T, &L.q_NW);
+  L.fwd_blocks = (n + L.fwd_R - 1) / L.fwd_R;
+  L.fwd_tiles = (n + L.fwd_T - 1) / L.fwd_T;
+  L.kv_blocks = (n + L.kv_R - 1) / L.kv_R;
+  L.kv_tiles = (n + L.kv_T - 1) / L.kv_T;
+  L.q_blocks = (n + L.q_R - 1) / L.q_R;
+  L.q_tiles = (n + L.q_T - 1) / L.q_T;
+  L.bitmap = align256((size_t)exattn::bitmap_words(n) * 4);
+  L.fwd = align256((size_t)L.fwd_blocks * (L.fwd_tiles + 1) * 4);
+  L.kv = align256((size_t)L.kv_blocks * (L.kv_tiles + 1) * 4);
+  L.q = align256((size_t)L.q_blocks * (L.q_tiles + 1) * 4);
+  L.rows = 2 * ws_region_bytes(B, H, n);
+  L.total = L.bitmap + L.fwd + L.kv + L.q + L.rows;
+  return L;
+}
+
+// Host-side checks of the pattern descriptor (its arrays stay on the device).
+int check_pattern(const exattn_pattern* pat, int n) {
+  if (pat == nullptr) return EXATTN_EINVAL;
+  if (pat->window < -1 || pat->n_global < 0) return EXATTN_EINVAL;
+  if (pat->n_global > 0 && (pat->global_idx == nullptr || ((uintptr_t)pat->global_idx & 3u))) return EXATTN_EINVAL;
+  if (pat->layout_block != 0 && pat->layout_block != exattn::kLayoutBlock) return EXATTN_EUNSUPPORTED;
+  if (pat->layout_block != 0 && pat->layout == nullptr) return EXATTN_EINVAL;
+  (void)n;
+  return EXATTN_OK;
+}
+
+size_t layout_bytes(const exattn_pattern* pat, int n) {
+  if (pat->layout_block == 0) return 0;
+  const size_t nb = (size_t)(n + exattn::kLayoutBlock - 1) / exattn::kLayoutBlock;
+  return nb * nb;
+}
+
+exattn::PlanInput plan_input(const exattn_pattern* pat, int n, void* workspace) {
+  exattn::PlanInput in{};
+  in.n = n;
+  in.window = pat->window;
+  in.n_global = pat->n_global;
+  in.global_idx = pat->global_idx;
+  in.layout = pat->layout_block ? pat->layout : nullptr;
+  in.layout_n = (n + exattn::kLayoutBlock - 1) / exattn::kLayoutBlock;
+  in.gbits = (uint32_t*)workspace;
+  return in;
+}
+
+// Builds one list in the region at `base`; returns the run-time descriptor.
+hipError_t build_list(const exattn::PlanInput& in, char* base, int R, int T, int NW, int blocks, int tiles,
+                      bool transposed, bool tail_partial, exattn::PatternDev* dev, hipStream_t s) {
+  exattn::PlanList pl{};
+  pl.R = R;
+  pl.T = T;
+  pl.NW = NW;
+  pl.transposed = transposed;
+  pl.tail_partial = tail_partial;
+  pl.count = (int*)base;
+  pl.list = (int*)base + blocks;
+  pl.stride = tiles;
+  pl.nblocks = blocks;
+  *dev = exattn::PatternDev{in.window, in.gbits, pl.list, pl.count, tiles};
+  return exattn::launch_pattern_list(in, pl, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_pattern_workspace_bytes(int dtype, int B, int H, int n, int d) {
+  if (check_problem(dtype, B, H, n, d, 1.0f, -1, H) != EXATTN_OK) return 0;
+  return pattern_layout(B, H, n, d).total;
+}
+
+int attn_fwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V, float scale,
+                     const exattn_pattern* pattern, void* O, float* LSE, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, -1, H);
+  if (st != EXATTN_OK) return st;
+  st = check_pattern(pattern, n);
+  if (st != EXATTN_OK) return st;
+  if (dtype != EXATTN_BF16) return EXATTN_EUNSUPPORTED;
+  const void* ptrs[] = {Q, K, V, O, LSE, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return EXATTN_EINVAL;
+  const PatternLayout L = pattern_layout(B, H, n, d);
+  if (workspace_bytes < L.total) return EXATTN_EWORKSPACE;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {pattern->global_idx, (size_t)pattern->n_global * 4},
+                      {pattern->layout, layout_bytes(pattern, n)}};
+  const Span outs[] = {{O, tb}, {LSE, lb}, {workspace, L.total}};
+  for (int o = 0; o < 3; ++o) {
+    for (const Span& in : ins)
+      if (in.n && overlaps(outs[o].p, outs[o].n, in.p, in.n)) return EXATTN_EINVAL;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o].p, outs[o].n, outs[o2].p, outs[o2].n)) return EXATTN_EINVAL;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const exattn::PlanInput in = plan_input(pattern, n, workspace);
+  hipError_t e = exattn::launch_pattern_bitmap(in, s);
+  exattn::FwdParams p{Q, K, V, O, LSE, B, H, n, d, scale, -1, 1};
+  if (e == hipSuccess)
+    e = build_list(in, (char*)workspace + L.bitmap, L.fwd_R, L.fwd_T, L.fwd_NW, L.fwd_blocks, L.fwd_tiles, false,
+                   true, &p.pattern, s);
+  if (e == hipSuccess) e = exattn::launch_fwd_bf16(p, s);
+  return from_hip(e);
+}
+
+int attn_bwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
+                     const void* O, const void* dO, const float* LSE, float scale, const exattn_pattern* pattern,
+                     void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(dtype, B, H, n, d, scale, -1, H);
+  if (st != EXATTN_OK) return st;
+  st = check_pattern(pattern, n);
+  if (st != EXATTN_OK) return st;
+  if (dtype != EXATTN_BF16) return EXATTN_EUNSUPPORTED;
+  const void* ptrs[] = {Q, K, V, O, dO, LSE, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return EXATTN_EINVAL;
+  const PatternLayout L = pattern_layout(B, H, n, d);
+  if (workspace_bytes < L.total) return EXATTN_EWORKSPACE;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {O, tb}, {dO, tb}, {LSE, lb},
+                      {pattern->global_idx, (size_t)pattern->n_global * 4}, {pattern->layout, layout_bytes(pattern, n)}};
+  const Span outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {workspace, L.total}};
+  for (int o = 0; o < 4; ++o) {
+    for (const Span& in : ins)
+      if (in.n && overlaps(outs[o].p, outs[o].n, in.p, in.n)) return EXATTN_EINVAL;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlaps(outs[o].p, outs[o].n, outs[o2].p, outs[o2].n)) return EXATTN_EINVAL;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const exattn::PlanInput in = plan_input(pattern, n, workspace);
+  char* base = (char*)workspace;
+  void* rows = base + L.bitmap + L.fwd + L.kv + L.q;
+  exattn::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, dQ, dK, dV, rows, B, H, n, d, scale, -1, 1);
+  hipError_t e = exattn::launch_pattern_bitmap(in, s);
+  if (e == hipSuccess)
+    e = build_list(in, base + L.bitmap + L.fwd, L.kv_R, L.kv_T, L.kv_NW, L.kv_blocks, L.kv_tiles, true, false,
+                   &p.pattern_kv, s);
+  if (e == hipSuccess)
+    e = build_list(in, base + L.bitmap + L.fwd + L.kv, L.q_R, L.q_T, L.q_NW, L.q_blocks, L.q_tiles, false, false,
+                   &p.pattern_q, s);
+  if (e == hipSuccess) e = exattn::launch_bwd_bf16(p, exattn::kStageAll, s);
+  return from_hip(e);
+}
+
+}  // extern "C"
+

@@ -21,6 +21,7 @@
 #include "bwd_common.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pattern.hpp"
 
 namespace exattn {
 namespace {
@@ -35,12 +36,16 @@ struct KvCfg {
   static constexpr int WPE = D == 256 ? 1 : 2;  // waves per SIMD
 };
 
-template <int D, bool WINDOWED>
+// MODE: kMaskNone, kMaskWindow (contiguous band of query tiles) or
+// kMaskPattern (the workgroup's tile list from the pattern plan).
+template <int D, int MODE>
 __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int n, int n_kblocks, int total_blocks, float scale,
-    float scale_log2, int window, int group) {
+    float scale_log2, int window, int group, PatternDev pat) {
+  constexpr bool WINDOWED = MODE == kMaskWindow;
+  constexpr bool PATTERN = MODE == kMaskPattern;
   constexpr int NW = KvCfg<D>::NW;
   constexpr int BQ = KvCfg<D>::BQ;
   constexpr int NT = NW * 64;
@@ -83,10 +88,22 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   int q_lo = 0, q_hi = n;
   if constexpr (WINDOWED) band_keys(kb0, kb0 + BKV, n, window, &q_lo, &q_hi);
   const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
-  // query rows that see this lane's key (the window is symmetric), within n
+  // query tiles visited: a contiguous range, or the pattern plan's list
+  const int* plist = PATTERN ? pat.list + (size_t)kblk * pat.stride : nullptr;
+  const int n_tiles = PATTERN ? pat.count[kblk] : t_hi - t_lo;
+  auto tile_at = [&](int i) { return PATTERN ? plist[i] >> kEntryTileShift : t_lo + i; };
+  // query rows that see this lane's key through the band (the window is
+  // symmetric), within n
   int row_lo = 0, row_hi = n;
   if constexpr (WINDOWED) band_keys(my_key, my_key + 1, n, window, &row_lo, &row_hi);
+  if constexpr (PATTERN) {
+    if (pat.window >= 0)
+      band_keys(my_key, my_key + 1, n, pat.window, &row_lo, &row_hi);
+    else
+      row_hi = row_lo;
+  }
   const unsigned row_span = (unsigned)max(row_hi - row_lo, 0);
+  const bool key_global = PATTERN && bit_of(pat.gbits, my_key);
 
   // Q and dO tiles, and the LSE*log2(e) and D values of their rows, go
   // straight from global memory to LDS.  Rows past n are clamped copies of
@@ -115,20 +132,21 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   }
 
   // One sweep over the band's query tiles per query head of the group.
-  const int steps = (t_hi - t_lo) * group;
-  if (steps > 0) load_tile(t_lo, 0, 0);
+  const int steps = n_tiles * group;
+  if (steps > 0) load_tile(tile_at(0), 0, 0);
   wait_all_and_barrier();
 
   int step = 0;
   for (int qg = 0; qg < group; ++qg)
-  for (int t = t_lo; t < t_hi; ++t, ++step) {
+  for (int it = 0; it < n_tiles; ++it, ++step) {
+    const int t = tile_at(it);
     const int buf = step & 1;
     // prefetch the next tile (the next head's first tile after the last one);
     // its buffer was released by the last barrier
-    if (t + 1 < t_hi)
-      load_tile(t + 1, qg, buf ^ 1);
+    if (it + 1 < n_tiles)
+      load_tile(tile_at(it + 1), qg, buf ^ 1);
     else if (qg + 1 < group)
-      load_tile(t_lo, qg + 1, buf ^ 1);
+      load_tile(tile_at(0), qg + 1, buf ^ 1);
     const __bf16* Qs = tiles[buf][0];
     const __bf16* dOs = tiles[buf][1];
     const int i0 = t * BQ;
@@ -142,11 +160,21 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
     }
 
     // With a window, queries outside this lane's key band get P = 0 (rows
-    // past n already have P = 0 through their LSE).
+    // past n already have P = 0 through their LSE).  Under a pattern, a
+    // partial tile keeps the pairs that the band, a global row, a global key
+    // or the layout make visible.
     bool need_mask = false;
+    uint32_t gq = 0;  // global bits of the tile's rows, shifted to this lane's half
     if constexpr (WINDOWED) {
       const int k_lo_w = kb0 + wave * 32;
       need_mask = max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
+    }
+    uint32_t any_key = 0;  // this lane's key is global, or the layout covers the wave
+    if constexpr (PATTERN) {
+      const int entry = plist[it];
+      need_mask = entry & 1;
+      any_key = (uint32_t)key_global | (uint32_t)((entry >> (1 + wave)) & 1);
+      gq = pat.gbits[t] >> (4 * hi);  // BQ = 32: one bitmap word per tile
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -159,6 +187,11 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
         float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j]));
         // queries that see this lane's key: [row_lo, row_lo + row_span)
         if (WINDOWED && need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
+        if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
+          const uint32_t vis = (uint32_t)((unsigned)(i0 + rb + j - row_lo) < row_span) | any_key |
+                               ((gq >> (8 * g + j)) & 1u);
+          p = vis ? p : 0.0f;
+        }
         s[r] = p;
         dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
       }
@@ -216,12 +249,14 @@ struct QCfg<256> {
   static constexpr int NW = 4, BC = 32, WPE = 1;
 };
 
-template <int D, bool WINDOWED>
+template <int D, int MODE>
 __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
     __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window,
-    int group) {
+    int group, PatternDev pat) {
+  constexpr bool WINDOWED = MODE == kMaskWindow;
+  constexpr bool PATTERN = MODE == kMaskPattern;
   constexpr int NW = QCfg<D>::NW;
   constexpr int BC = QCfg<D>::BC;
   constexpr int NT = NW * 64;
@@ -263,10 +298,21 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
   int k_lo = 0, k_hi = n;
   if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
   const int t_lo = k_lo / BC, t_hi = (k_hi + BC - 1) / BC;
-  // keys visible to this lane's row
+  // key tiles visited: a contiguous range, or the pattern plan's list
+  const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
+  const int n_tiles = PATTERN ? pat.count[qb] : t_hi - t_lo;
+  auto tile_at = [&](int i) { return PATTERN ? plist[i] >> kEntryTileShift : t_lo + i; };
+  // keys visible to this lane's row through the band
   int key_lo = 0, key_hi = n;
   if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
+  if constexpr (PATTERN) {
+    if (pat.window >= 0)
+      band_keys(my_row, my_row + 1, n, pat.window, &key_lo, &key_hi);
+    else
+      key_hi = key_lo;
+  }
   const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
+  const bool row_global = PATTERN && bit_of(pat.gbits, my_row);
 
   // K and V tiles go straight from global memory to LDS.  Key rows past n
   // are zeros in the K tile, so whatever their dS, they add exactly nothing
@@ -283,13 +329,13 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
-  if (t_lo < t_hi) load_tile(t_lo, 0);
+  if (n_tiles > 0) load_tile(tile_at(0), 0);
   wait_all_and_barrier();
 
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1, buf ^ 1);  // buffer released by the last barrier
+  for (int it = 0; it < n_tiles; ++it) {
+    const int t = tile_at(it);
+    const int buf = it & 1;
+    if (it + 1 < n_tiles) load_tile(tile_at(it + 1), buf ^ 1);  // buffer released by the last barrier
     const __bf16* Ks = tiles[buf][0];
     const __bf16* Vs = tiles[buf][1];
     const int kbase = t * BC;
@@ -308,11 +354,18 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
     }
 
     // With a window, keys outside this lane's row band get P = 0 (keys past
-    // n meet zero K rows).
+    // n meet zero K rows).  Under a pattern, a partial tile keeps the pairs
+    // that the band, a global row, a global key or the layout make visible.
     bool need_mask = false;
+    uint32_t any_row = 0;  // this lane's row is global, or the layout covers the wave
     if constexpr (WINDOWED) {
       const int r_lo = q0 + wave * 32;
       need_mask = max(r_lo + 31 - kbase, kbase + BC - 1 - r_lo) > window;
+    }
+    if constexpr (PATTERN) {
+      const int entry = plist[it];
+      need_mask = entry & 1;
+      any_row = (uint32_t)row_global | (uint32_t)((entry >> (1 + wave)) & 1);
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -322,6 +375,13 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
         if (WINDOWED && need_mask) {
           const int key = kbase + kb * 32 + acc_row(r, lane);
           p = (unsigned)(key - key_lo) < key_span ? p : 0.0f;
+        }
+        if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
+          const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
+          const int key = kbase + kb * 32 + e + 4 * hi;
+          const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);
+          const uint32_t vis = (uint32_t)((unsigned)(key - key_lo) < key_span) | any_row | ((gk >> e) & 1u);
+          p = vis ? p : 0.0f;
         }
         dp[kb][r] = p * (dp[kb][r] - dl);  // dS^T (unscaled)
       }
@@ -352,7 +412,7 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
   }
 }
 
-template <int D, bool W>
+template <int D, int W>
 hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const float scale_log2 = p.scale * kLog2e;
   const long heads = (long)p.B * p.H;
@@ -374,29 +434,50 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(KvCfg<D>::NW * 64), 0, stream,
                        (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
                        p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window,
-                       p.group);
+                       p.group, p.pattern_kv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageQ) {
     hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(QCfg<D>::NW * 64), 0, stream,
                        (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
-                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group);
+                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group,
+                       p.pattern_q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+template <int MODE>
+hipError_t bwd_mode(const BwdParams& p, unsigned stages, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return bwd_d<64, MODE>(p, stages, stream);
+    case 128: return bwd_d<128, MODE>(p, stages, stream);
+    case 256: return bwd_d<256, MODE>(p, stages, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stream) {
-  const bool w = p.window >= 0;
-  switch (p.d) {
-    case 64: return w ? bwd_d<64, true>(p, stages, stream) : bwd_d<64, false>(p, stages, stream);
-    case 128: return w ? bwd_d<128, true>(p, stages, stream) : bwd_d<128, false>(p, stages, stream);
-    case 256: return w ? bwd_d<256, true>(p, stages, stream) : bwd_d<256, false>(p, stages, stream);
-    default: return hipErrorInvalidValue;
+  if (p.pattern_kv.list != nullptr) return bwd_mode<kMaskPattern>(p, stages, stream);
+  return p.window >= 0 ? bwd_mode<kMaskWindow>(p, stages, stream) : bwd_mode<kMaskNone>(p, stages, stream);
+}
+
+void bwd_kv_bf16_geometry(int d, int* keys_per_block, int* rows_per_tile, int* waves) {
+  const int nw = d == 64 ? KvCfg<64>::NW : d == 128 ? KvCfg<128>::NW : KvCfg<256>::NW;
+  *keys_per_block = 32 * nw;
+  *rows_per_tile = KvCfg<128>::BQ;
+  *waves = nw;
+}
+
+void bwd_q_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves) {
+  switch (d) {
+    case 64: *rows_per_block = 32 * QCfg<64>::NW; *keys_per_tile = QCfg<64>::BC; *waves = QCfg<64>::NW; break;
+    case 128: *rows_per_block = 32 * QCfg<128>::NW; *keys_per_tile = QCfg<128>::BC; *waves = QCfg<128>::NW; break;
+    default: *rows_per_block = 32 * QCfg<256>::NW; *keys_per_tile = QCfg<256>::BC; *waves = QCfg<256>::NW; break;
   }
 }
 

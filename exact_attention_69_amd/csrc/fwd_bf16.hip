@@ -29,6 +29,7 @@
 // Scores are handled in the base-2 domain: exp(scale*s) = 2^(scale*log2e*s).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pattern.hpp"
 
 namespace exattn {
 namespace {
@@ -56,11 +57,16 @@ struct FwdCfg<256> {
   static constexpr int NW = 4, RB = 1, BC = 32, WPE = 1;
 };
 
-template <int D, bool WINDOWED>
+// MODE: kMaskNone, kMaskWindow (contiguous band of key tiles, analytic
+// masks), or kMaskPattern (the workgroup's tile list from the pattern plan;
+// the union mask on partial tiles).
+template <int D, int MODE>
 __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n_qblocks, int total_blocks,
-    float scale_log2, int window, int group) {
+    float scale_log2, int window, int group, PatternDev pat) {
+  constexpr bool WINDOWED = MODE == kMaskWindow;
+  constexpr bool PATTERN = MODE == kMaskPattern;
   constexpr int NW = FwdCfg<D>::NW;
   constexpr int RB = FwdCfg<D>::RB;
   constexpr int BC = FwdCfg<D>::BC;
@@ -108,18 +114,32 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
       qreg[rb][ds] = __builtin_bit_cast(bf16x8, ok ? src[2 * ds] : u32x4{0, 0, 0, 0});
   }
 
-  // Key tiles this block visits (band of the whole block for a window).
+  // Key tiles this block visits: a contiguous range (the band of the whole
+  // block for a window), or the block's list from the pattern plan.
   int k_lo = 0, k_hi = n;
   if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
   const int t_lo = k_lo / BC;
   const int t_hi = (k_hi + BC - 1) / BC;
-  // keys visible to each of this lane's rows
+  const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
+  const int n_tiles = PATTERN ? pat.count[qb] : t_hi - t_lo;
+  auto tile_at = [&](int i) { return PATTERN ? plist[i] >> kEntryTileShift : t_lo + i; };
+  // keys visible to each of this lane's rows through the band
   int key_lo[RB];
   unsigned key_span[RB];
+  bool row_global[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     int lo = 0, hi_k = n;
     if constexpr (WINDOWED) band_keys(my_row[rb], my_row[rb] + 1, n, window, &lo, &hi_k);
+    if constexpr (PATTERN) {
+      if (pat.window >= 0)
+        band_keys(my_row[rb], my_row[rb] + 1, n, pat.window, &lo, &hi_k);
+      else
+        hi_k = lo;  // no band term
+      row_global[rb] = bit_of(pat.gbits, my_row[rb]);
+    } else {
+      row_global[rb] = false;
+    }
     key_lo[rb] = lo;
     key_span[rb] = (unsigned)max(hi_k - lo, 0);
   }
@@ -158,30 +178,54 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
 
   // Prologue: K and V of the first tile, K of the second.  Key rows past n
   // are clamped copies; their scores are masked to -inf (P = 0).
-  if (t_lo < t_hi) {
-    Tile::issue(K + (size_t)t_lo * BC * D, n - t_lo * BC, kbuf[0], tid);
-    Tile::issue(V + (size_t)t_lo * BC * D, n - t_lo * BC, vbuf[0], tid);
-    if (t_lo + 1 < t_hi) Tile::issue(K + (size_t)(t_lo + 1) * BC * D, n - (t_lo + 1) * BC, kbuf[1], tid);
+  auto issue_k = [&](int t, __bf16* buf) { Tile::issue(K + (size_t)t * BC * D, n - t * BC, buf, tid); };
+  auto issue_v = [&](int t, __bf16* buf) { Tile::issue(V + (size_t)t * BC * D, n - t * BC, buf, tid); };
+  if (n_tiles > 0) {
+    issue_k(tile_at(0), kbuf[0]);
+    issue_v(tile_at(0), vbuf[0]);
+    if (n_tiles > 1) issue_k(tile_at(1), kbuf[1]);
   }
   wait_all_and_barrier();
   f32x16 s_cur[RB][NKB];
   compute_s(kbuf[0], s_cur);
 
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int j = t - t_lo;
-    // V of tile t+1 into the V buffer read last iteration, K of tile t+2 into
+  for (int j = 0; j < n_tiles; ++j) {
+    const int t = tile_at(j);
+    // V of tile j+1 into the V buffer read last iteration, K of tile j+2 into
     // the K buffer read last iteration (both released by the last barrier).
-    if (t + 1 < t_hi) Tile::issue(V + (size_t)(t + 1) * BC * D, n - (t + 1) * BC, vbuf[(j + 1) & 1], tid);
-    if (t + 2 < t_hi) Tile::issue(K + (size_t)(t + 2) * BC * D, n - (t + 2) * BC, kbuf[j & 1], tid);
+    if (j + 1 < n_tiles) issue_v(tile_at(j + 1), vbuf[(j + 1) & 1]);
+    if (j + 2 < n_tiles) issue_k(tile_at(j + 2), kbuf[j & 1]);
     const int kbase = t * BC;
 
-    // ---- masks: key tail and sliding window (branch-free range test) -------
+    // ---- masks: key tail, sliding window, pattern ---------------------------
     bool need_mask = kbase + BC > n;
     if constexpr (WINDOWED) {
       const int r_hi = w0 + 32 * RB - 1;
       need_mask = need_mask || max(r_hi - kbase, kbase + BC - 1 - w0) > window;
     }
-    if (need_mask) {
+    if constexpr (PATTERN) {
+      const int entry = plist[j];
+      if (entry & 1) {
+        static_assert(RB == 1 && BC % 32 == 0, "pattern masks assume one 32-row block per wave");
+        // visible: key < n and (band or global row or global key or the
+        // layout covers this wave's rows for the tile).  Evaluated with
+        // bitwise operators into one select per element: no short-circuit
+        // branches.
+        const uint32_t any_row = (uint32_t)row_global[0] | (uint32_t)((entry >> (1 + wave)) & 1);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);  // keys kbase+32kb+4hi+..
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
+            const int key = kbase + kb * 32 + e + 4 * hi;
+            const uint32_t vis = (uint32_t)(key < n) &
+                                 ((uint32_t)((unsigned)(key - key_lo[0]) < key_span[0]) | any_row | ((gk >> e) & 1u));
+            s_cur[0][kb][r] = vis ? s_cur[0][kb][r] : kNegInf;
+          }
+        }
+      }
+    } else if (need_mask) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -274,11 +318,13 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -----------------------
+  // A row that saw no key (possible only under a pattern without a window)
+  // gets O = 0 and LSE = -inf.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = pair_sum(l_part[rb]);
     if (my_row[rb] < n) {
-      const float inv = 1.0f / l_tot;
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       __bf16* Orow = Og + head_off + (size_t)my_row[rb] * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -290,33 +336,46 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
           w[1] = pack_bf16x2(o[rb][db][4 * g + 2] * inv, o[rb][db][4 * g + 3] * inv);
           *(u32x2*)(Orow + dd) = w;
         }
-      if (hi == 0) LSEg[(size_t)head * n + my_row[rb]] = kLn2 * (m_run[rb] + fast_log2(l_tot));
+      if (hi == 0) LSEg[(size_t)head * n + my_row[rb]] = l_tot > 0.0f ? kLn2 * (m_run[rb] + fast_log2(l_tot)) : kNegInf;
     }
   }
 }
 
-template <int D, bool W>
+template <int D, int MODE>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   constexpr int BR = 32 * FwdCfg<D>::RB * FwdCfg<D>::NW;
   const int nqb = (p.n + BR - 1) / BR;
   const long total = (long)nqb * p.B * p.H;
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
   const float scale_log2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, W>), dim3((unsigned)total), dim3(FwdCfg<D>::NW * 64), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE>), dim3((unsigned)total), dim3(FwdCfg<D>::NW * 64), 0, stream,
                      (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (__bf16*)p.o, p.lse, p.n,
-                     nqb, (int)total, scale_log2, p.window, p.group);
+                     nqb, (int)total, scale_log2, p.window, p.group, p.pattern);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const FwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return launch_d<64, MODE>(p, stream);
+    case 128: return launch_d<128, MODE>(p, stream);
+    case 256: return launch_d<256, MODE>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  const bool w = p.window >= 0;
-  switch (p.d) {
-    case 64: return w ? launch_d<64, true>(p, stream) : launch_d<64, false>(p, stream);
-    case 128: return w ? launch_d<128, true>(p, stream) : launch_d<128, false>(p, stream);
-    case 256: return w ? launch_d<256, true>(p, stream) : launch_d<256, false>(p, stream);
-    default: return hipErrorInvalidValue;
+  if (p.pattern.list != nullptr) return launch_mode<kMaskPattern>(p, stream);
+  return p.window >= 0 ? launch_mode<kMaskWindow>(p, stream) : launch_mode<kMaskNone>(p, stream);
+}
+
+void fwd_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves) {
+  switch (d) {
+    case 64: *rows_per_block = 32 * FwdCfg<64>::NW; *keys_per_tile = FwdCfg<64>::BC; *waves = FwdCfg<64>::NW; break;
+    case 128: *rows_per_block = 32 * FwdCfg<128>::NW; *keys_per_tile = FwdCfg<128>::BC; *waves = FwdCfg<128>::NW; break;
+    default: *rows_per_block = 32 * FwdCfg<256>::NW; *keys_per_tile = FwdCfg<256>::BC; *waves = FwdCfg<256>::NW; break;
   }
 }
 

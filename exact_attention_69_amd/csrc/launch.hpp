@@ -4,7 +4,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pattern.hpp"
+
 namespace exattn {
+
+// Masking modes of the kernels.
+enum MaskMode : int { kMaskNone = 0, kMaskWindow = 1, kMaskPattern = 2 };
 
 struct FwdParams {
   const void* q;
@@ -16,6 +21,7 @@ struct FwdParams {
   float scale;
   int window;  // -1: no mask
   int group;   // query heads per key/value head: K, V are [B, H / group, n, d]
+  PatternDev pattern;  // list == nullptr: no pattern
 };
 
 struct BwdParams {
@@ -34,9 +40,15 @@ struct BwdParams {
   float scale;
   int window;
   int group;  // query heads per key/value head: K, V, dK, dV are [B, H / group, n, d]
+  PatternDev pattern_kv;  // lists for the key-side pass (list == nullptr: no pattern)
+  PatternDev pattern_q;   // lists for the query-side pass
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+// Workgroup geometry of the bf16 kernels, for the pattern plan.
+void fwd_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves);
+void bwd_kv_bf16_geometry(int d, int* keys_per_block, int* rows_per_tile, int* waves);
+void bwd_q_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 // Backward stages: rowdot (D), key side (dK, dV), query side (dQ).
 enum BwdStage : unsigned { kStageRowdot = 1, kStageKV = 2, kStageQ = 4, kStageAll = 7 };

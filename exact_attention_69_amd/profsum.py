@@ -32,7 +32,8 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 KERNEL_RE = re.compile(r"(fwd_bf16_kernel|bwd_kv_bf16_kernel|bwd_q_bf16_kernel|bwd_rowdot_kernel|fwd_f32_kernel|"
-                       r"bwd_kv_f32_kernel|bwd_q_f32_kernel|elementwise_kernel|copy\w*)(?:I\w*?Li(\d+))?")
+                       r"bwd_kv_f32_kernel|bwd_q_f32_kernel|pattern_bitmap_kernel|pattern_list_kernel|elementwise_kernel|"
+                       r"copy\w*)(?:I\w*?Li(\d+))?")
 
 
 def short(name):

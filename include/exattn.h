@@ -212,6 +212,70 @@ int attn_bwd_dq_gqa(int dtype, int B, int H, int Hkv, int n, int d,
                     const void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/*
+ * Sparse attention patterns (the Longformer and BigBird patterns of the
+ * llmis.ru chapter 3.1 "The cost of attention", section 3).  The pattern is
+ * the union of three parts, shared by every (batch, head):
+ *   - a sliding window: row i sees key j when |i - j| <= window
+ *     (window = -1: no window part);
+ *   - global tokens: a global position attends to every key, and every
+ *     query attends to it (Longformer's task tokens);
+ *   - a block layout: with 64-token blocks, row i sees key j when
+ *     layout[(i / 64) * nb + j / 64] != 0, nb = ceil(n / 64) (BigBird's
+ *     local, global and random blocks are all entries of the layout; random
+ *     blocks are drawn by the caller).
+ * Attention over the pattern is the softmax over the visible keys only.  A
+ * row that sees no key (possible only without a window) gets O = 0 and
+ * LSE = -inf and contributes no gradient.
+ *
+ * The descriptor is read on the host; its arrays are DEVICE pointers:
+ *   global_idx : n_global int32 positions (any order; duplicates allowed;
+ *                positions outside [0, n) are ignored), 4-byte aligned.
+ *   layout     : nb * nb bytes, row-major (ignored when layout_block = 0).
+ */
+typedef struct {
+  int window;                  /* >= 0: band half-width; -1: no band part */
+  int n_global;                /* number of global positions (0: none) */
+  const int *global_idx;       /* device: the global positions */
+  int layout_block;            /* 0: no layout; 64: block layout present */
+  const unsigned char *layout; /* device: nb x nb block layout */
+} exattn_pattern;
+
+/*
+ * Workspace for attn_fwd_pattern and attn_bwd_pattern: the global-token
+ * bitmap, each kernel's per-workgroup tile lists (built on the device by
+ * every call, in stream order, before the attention kernels), and the
+ * backward's row arrays.  Returns 0 for arguments the calls would reject.
+ */
+size_t attn_pattern_workspace_bytes(int dtype, int B, int H, int n, int d);
+
+/*
+ * Forward and backward over a sparse pattern; arguments as for attn_fwd and
+ * attn_bwd (multi-head layout [B, H, n, d]), with the pattern in place of
+ * the window.  Only EXATTN_BF16 is supported (EXATTN_EUNSUPPORTED for f32).
+ * The workgroups visit only the tiles that hold a visible pair; tiles the
+ * pattern covers completely run unmasked.  The backward's O and LSE must
+ * come from attn_fwd_pattern with the same pattern.  Besides the errors of
+ * attn_fwd / attn_bwd: EXATTN_EINVAL for a NULL descriptor, window < -1,
+ * n_global < 0, a NULL or misaligned global_idx with n_global > 0, a NULL
+ * layout with layout_block = 64, or an output overlapping global_idx or
+ * layout; EXATTN_EUNSUPPORTED for a layout_block other than 0 or 64.
+ */
+int attn_fwd_pattern(int dtype, int B, int H, int n, int d,
+                     const void *Q, const void *K, const void *V,
+                     float scale, const exattn_pattern *pattern,
+                     void *O, float *LSE,
+                     void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+int attn_bwd_pattern(int dtype, int B, int H, int n, int d,
+                     const void *Q, const void *K, const void *V,
+                     const void *O, const void *dO, const float *LSE,
+                     float scale, const exattn_pattern *pattern,
+                     void *dQ, void *dK, void *dV,
+                     void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *exattn_status_string(int status);
 

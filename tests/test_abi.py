@@ -37,9 +37,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dkdv_gqa", "attn_bwd_dq",
-                                    "attn_bwd_dq_gqa", "attn_bwd_gqa", "attn_bwd_rowdot",
-                                    "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_gqa",
-                                    "exattn_status_string"]
+                                    "attn_bwd_dq_gqa", "attn_bwd_gqa", "attn_bwd_pattern", "attn_bwd_rowdot",
+                                    "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_gqa", "attn_fwd_pattern",
+                                    "attn_pattern_workspace_bytes", "exattn_status_string"]
 
 
 def test_binding_wraps_every_declared_symbol():
@@ -182,6 +182,38 @@ def test_gqa_overlap_checks_use_the_kv_size(lib):
     assert lib.attn_bwd_gqa(1, 1, H, Hkv, n, d, q, k, v, o, do, lse, 0.1, -1, dq, after, dv, ws, need - 1,
                             None) == EWORKSPACE
     assert lib.attn_fwd_gqa(1, 1, H, Hkv, n, d, q, k, v, 0.1, -1, inside, lse, None) == EINVAL
+
+
+def _pat(window=-1, n_global=0, gidx=None, block=0, layout=None):
+    import exact_attention_69_amd._binding as b
+    return b.ExattnPatternC(window, n_global, gidx, block, layout)
+
+
+def test_pattern_entry_points_reject_bad_arguments(lib):
+    n, d = 256, 64
+    need = lib.attn_pattern_workspace_bytes(1, 1, 2, n, d)
+    assert need > 0 and lib.attn_pattern_workspace_bytes(1, 1, 2, n, 80) == 0
+    q, k, v, o, lse, ws, gidx, lay = ptrs(8)
+    f = lambda pat, dtype=1, wsb=need, out=o: lib.attn_fwd_pattern(dtype, 1, 2, n, d, q, k, v, 0.1,
+                                                                   ctypes.byref(pat) if pat else None, out, lse,
+                                                                   ws, wsb, None)
+    good = _pat(3, 4, gidx, 64, lay)
+    assert f(None) == EINVAL
+    assert f(_pat(window=-2)) == EINVAL
+    assert f(_pat(n_global=-1)) == EINVAL
+    assert f(_pat(n_global=3, gidx=None)) == EINVAL
+    assert f(_pat(n_global=3, gidx=ctypes.c_void_p(gidx.value + 2))) == EINVAL  # misaligned
+    assert f(_pat(block=32, layout=lay)) == EUNSUPPORTED
+    assert f(_pat(block=64, layout=None)) == EINVAL
+    assert f(good, dtype=0) == EUNSUPPORTED
+    assert f(good, wsb=need - 1) == EWORKSPACE
+    assert f(good, out=ctypes.c_void_p(lay.value + 4)) == EINVAL  # O overlaps the layout
+    dq, dk, dv, do = ptrs(12)[8:]
+    bw = lambda pat, wsb=need: lib.attn_bwd_pattern(1, 1, 2, n, d, q, k, v, o, do, lse, 0.1,
+                                                    ctypes.byref(pat) if pat else None, dq, dk, dv, ws, wsb, None)
+    assert bw(None) == EINVAL
+    assert bw(good, wsb=need - 1) == EWORKSPACE
+    assert bw(_pat(window=-5)) == EINVAL
 
 
 def test_binding_rejects_host_tensors():

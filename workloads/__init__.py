@@ -16,6 +16,14 @@ on its own without drawing the whole problem):
   oracle upcasts the very values the GPU receives.
 * grouped-query workloads (``kv_heads`` < H): K and V are drawn for heads
   ``h < kv_heads`` only, with the same per-(b, h) streams.
+* sparse-pattern workloads: global token positions are the first
+  ``n_global // 2`` positions plus the rest drawn without replacement from
+  the remaining positions (``SeedSequence([seed, 100])``); a BigBird layout
+  ``(local, global, random)`` over 64-token blocks sets the blocks within
+  ``local // 2`` of the diagonal, every block of the first ``global`` block
+  rows and columns, and, in every other block row, ``random`` further blocks
+  drawn without replacement from the unset ones (``SeedSequence([seed, 200,
+  row])``).  The same arrays go to the GPU and to the oracle.
 """
 
 from dataclasses import dataclass, field
@@ -31,6 +39,9 @@ __all__ = [
     "draw_head",
     "draw_inputs",
     "pair_count",
+    "draw_pattern",
+    "pattern_pair_count",
+    "LAYOUT_BLOCK",
 ]
 
 TENSORS = ("q", "k", "v", "do")
@@ -51,7 +62,13 @@ class Workload:
     q_mult: float = 1.0
     seed: int = 69000
     kv_heads: int = 0  # 0: one key/value head per query head
+    n_global: int = 0  # sparse pattern: number of global tokens
+    bigbird: tuple = ()  # sparse pattern: (local, global, random) blocks of 64
     note: str = field(default="", compare=False)
+
+    @property
+    def has_pattern(self):
+        return self.n_global > 0 or bool(self.bigbird)
 
     @property
     def scale(self):
@@ -89,7 +106,57 @@ WORKLOADS = [
 VARIANTS = [
     Workload("bf16_b2h32kv8_n8192_d128_gqa", 2, 32, 8192, 128, "bf16", seed=69006, kv_heads=8,
              note="grouped-query: 8 key/value heads, each shared by 4 query heads"),
+    Workload("bf16_b1h16_n16384_d128_longformer_w256_g16", 1, 16, 16384, 128, "bf16", window=256, seed=69007,
+             n_global=16, note="Longformer: window |i-j|<=256 plus 16 global tokens"),
+    Workload("bf16_b1h16_n16384_d128_bigbird_b64", 1, 16, 16384, 128, "bf16", seed=69008, bigbird=(3, 2, 3),
+             note="BigBird: 64-token blocks, 3 local, 2 global, 3 random per block row"),
 ]
+
+LAYOUT_BLOCK = 64
+
+
+def draw_pattern(wl):
+    """(window, global positions int32 sorted, layout uint8 [nb, nb] or None)
+    of a sparse-pattern workload (recipe in the module docstring)."""
+    n = wl.n
+    glob = np.zeros(0, dtype=np.int32)
+    if wl.n_global:
+        head = np.arange(wl.n_global // 2)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 100])))
+        rest = g.choice(np.arange(wl.n_global // 2, n), size=wl.n_global - wl.n_global // 2, replace=False)
+        glob = np.sort(np.concatenate([head, rest])).astype(np.int32)
+    layout = None
+    if wl.bigbird:
+        local, nglob, nrand = wl.bigbird
+        nb = -(-n // LAYOUT_BLOCK)
+        i = np.arange(nb)
+        layout = (np.abs(i[:, None] - i[None, :]) <= local // 2)
+        layout[:nglob, :] = True
+        layout[:, :nglob] = True
+        for r in range(nglob, nb):
+            free = np.flatnonzero(~layout[r])
+            g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 200, r])))
+            pick = g.choice(free, size=min(nrand, free.size), replace=False)
+            layout[r, pick] = True
+        layout = layout.astype(np.uint8)
+    return wl.window, glob, layout
+
+
+def pattern_pair_count(n, window, global_idx, layout, row_block=1024):
+    """Visible (query, key) pairs of a sparse pattern (for FLOP counts)."""
+    isg = np.zeros(n, dtype=bool)
+    isg[np.asarray(global_idx, dtype=np.int64)] = True
+    cols = np.arange(n)
+    total = 0
+    for r0 in range(0, n, row_block):
+        rows = np.arange(r0, min(n, r0 + row_block))
+        vis = isg[rows][:, None] | isg[None, :]
+        if window >= 0:
+            vis = vis | (np.abs(rows[:, None] - cols[None, :]) <= window)
+        if layout is not None:
+            vis = vis | layout.astype(bool)[rows // LAYOUT_BLOCK][:, cols // LAYOUT_BLOCK]
+        total += int(vis.sum())
+    return total
 
 
 def workload(name_or_index):
