@@ -24,6 +24,13 @@ from .attention import (  # noqa: F401
     forward_rows,
     backward_dq_rows,
 )
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_round,
+    fwht_f32,
+    quantize_head,
+    attention_forward_fp8,
+)
 from .pattern import (  # noqa: F401
     Pattern,
     attention_forward_pattern,
