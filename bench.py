@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak at n=8192, d=128 (1 GPU)"
 DEFAULT_WORKLOAD = "bf16_b2h32_n8192_d128_q3"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -42,7 +42,8 @@ _PAIRS = {}
 
 def flops(wl, pairs=False):
     """Algorithmic (fwd, bwd) FLOPs: 4 and 10 x visible pairs x d, over all
-    heads; with pairs=True, the visible (query, key) pairs of one head."""
+    heads (FP8 workloads: forward only); with pairs=True, the visible
+    (query, key) pairs of one head."""
     from workloads import draw_pattern, pair_count, pattern_pair_count
     if wl.name not in _PAIRS:
         if wl.has_pattern:
@@ -53,7 +54,7 @@ def flops(wl, pairs=False):
     if pairs:
         return _PAIRS[wl.name]
     p = _PAIRS[wl.name] * wl.B * wl.H
-    return 4.0 * p * wl.d, 10.0 * p * wl.d
+    return 4.0 * p * wl.d, 0.0 if wl.fp8 else 10.0 * p * wl.d
 
 
 def hbm_bytes(wl):
@@ -64,6 +65,9 @@ def hbm_bytes(wl):
     t = wl.B * wl.H * wl.n * wl.d * eb
     tkv = wl.B * wl.Hkv * wl.n * wl.d * eb
     r = wl.B * wl.H * wl.n * 4
+    if wl.fp8:  # E4M3 Q, K, V in; bf16 O and fp32 LSE out; forward only
+        t8 = wl.B * wl.H * wl.n * wl.d
+        return 3 * t8 + 2 * t8 + r, 0
     return 2 * t + 2 * tkv + r, 4 * t + 4 * tkv + 3 * r
 
 
@@ -146,7 +150,18 @@ def time_steps(wl, steps, warmup):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     code = ea.EXATTN_BF16 if wl.dtype == "bf16" else ea.EXATTN_F32
     stream = torch.cuda.current_stream(dev)
-    if wl.has_pattern:
+    if wl.fp8:
+        from workloads import draw_signs
+        sg = torch.from_numpy(draw_signs(wl)).to(dev) if wl.rotate else None
+        # inputs quantised once (E4M3 codes resident in HBM); the timed call
+        # is the FP8 forward
+        q8, qs = ea.attn_quant_fp8(q, sg, ea.EXATTN_FP8_ROWS, stream=stream)
+        k8, ks = ea.attn_quant_fp8(k, sg, ea.EXATTN_FP8_ROWS, stream=stream)
+        v8, vs = ea.attn_quant_fp8(v, None, ea.EXATTN_FP8_V_TRANSPOSED, stream=stream)
+        names = [f"fwd_fp8_kernel<{wl.d}>"]
+        calls = (lambda: ea.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, q.shape, wl.scale, rotated=wl.rotate, out=o,
+                                         lse=lse, stream=stream),)
+    elif wl.has_pattern:
         window, glob, layout = draw_pattern(wl)
         pat = ea.AttnPattern(window, torch.from_numpy(glob).to(dev) if len(glob) else None,
                              torch.from_numpy(layout).to(dev) if layout is not None else None)
@@ -246,7 +261,11 @@ def main(argv=None):
             entry = {"value": round((vf + vb) / (vms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                      "ms_per_step": round(vms, 4), "steps": args.variant_steps, "B": vw.B, "H": vw.H, "Hkv": vw.Hkv,
                      "n": vw.n, "d": vw.d, "window": vw.window, "kernel_ms": {vn[i]: round(vk[i], 4) for i in range(len(vn))}}
-            if vw.has_pattern:
+            if vw.fp8:
+                entry.update(rotated=vw.rotate, peak_tflops=PEAK_TFLOPS["fp8"],
+                             pct_fp8_peak=round(100.0 * (vf / (vms * 1e-3) / 1e12) / PEAK_TFLOPS["fp8"], 2),
+                             note="FP8 forward on E4M3 inputs quantised beforehand (O bf16)")
+            elif vw.has_pattern:
                 entry.update(n_global=vw.n_global, bigbird=list(vw.bigbird), visible_pairs_per_head=flops(vw, pairs=True),
                              fwd_tflops=round(vf / (vk[0] * 1e-3) / 1e12, 2),
                              bwd_tflops=round(vb / (vk[1] * 1e-3) / 1e12, 2))

@@ -7,6 +7,8 @@ include/exattn.h); this package only marshals PyTorch device tensors into it.
 from ._binding import (  # noqa: F401
     EXATTN_BF16,
     EXATTN_F32,
+    EXATTN_FP8_ROWS,
+    EXATTN_FP8_V_TRANSPOSED,
     AttnPattern,
     ExattnError,
     LIB_PATH,
@@ -20,9 +22,12 @@ from ._binding import (  # noqa: F401
     attn_bwd_rowdot,
     attn_bwd_workspace_bytes,
     attn_fwd,
+    attn_fp8_bytes,
+    attn_fwd_fp8,
     attn_fwd_gqa,
     attn_fwd_pattern,
     attn_pattern_workspace_bytes,
+    attn_quant_fp8,
     exattn_status_string,
     load_library,
 )

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libexattn.so")
 
 EXATTN_F32 = 0
 EXATTN_BF16 = 1
+EXATTN_FP8_ROWS = 0
+EXATTN_FP8_V_TRANSPOSED = 1
 STATUS = {0: "EXATTN_OK", -1: "EXATTN_EINVAL", -2: "EXATTN_EUNSUPPORTED", -3: "EXATTN_EWORKSPACE", -4: "EXATTN_EHIP"}
 
 _lib = None
@@ -97,6 +99,13 @@ def load_library(path=None):
     lib.attn_fwd_pattern.restype = ci
     lib.attn_bwd_pattern.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, pp, vp, vp, vp, vp, cs, vp]
     lib.attn_bwd_pattern.restype = ci
+    lib.attn_fp8_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.attn_fp8_bytes.restype = cs
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.attn_quant_fp8.argtypes = [ci, ci, ci, ci, vp, vp, ci, vp, vp, vp]
+    lib.attn_quant_fp8.restype = ci
+    lib.attn_fwd_fp8.argtypes = [ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp]
+    lib.attn_fwd_fp8.restype = ci
     lib.exattn_status_string.argtypes = [ci]
     lib.exattn_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -392,3 +401,49 @@ def attn_bwd_pattern(q, k, v, o, do, lse, pattern, scale=None, workspace=None, d
           do.data_ptr(), lse.data_ptr(), scale, ctypes.byref(pc), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
           workspace.data_ptr(), wsb, (q.device, _stream_ptr(q, stream)))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) forward and its quantiser
+# ---------------------------------------------------------------------------
+
+def attn_fp8_bytes(B, H, n, d, layout):
+    return int(load_library().attn_fp8_bytes(B, H, n, d, layout))
+
+
+def attn_quant_fp8(x, signs=None, layout=EXATTN_FP8_ROWS, stream=None):
+    """Quantise a bf16 [B, H, n, d] tensor to E4M3 codes (uint8 tensor in
+    the requested layout) and per-head scales (float32 [B, H])."""
+    torch = _torch()
+    _check_inputs(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("attn_quant_fp8 takes bfloat16 input")
+    B, H, n, d = x.shape
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d or not signs.is_cuda):
+        raise ValueError("signs must be a float32 GPU tensor of d entries (+1 or -1)")
+    x8 = torch.empty(max(attn_fp8_bytes(B, H, n, d, layout), 1), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    _call("attn_quant_fp8", B, H, n, d, x.data_ptr(), None if signs is None else signs.data_ptr(), int(layout),
+          x8.data_ptr(), scale.data_ptr(), (x.device, _stream_ptr(x, stream)))
+    return x8, scale
+
+
+def attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, shape, scale=None, rotated=False, out=None, lse=None,
+                 stream=None):
+    """FP8 forward on quantised inputs (from attn_quant_fp8; V in the
+    transposed layout).  `shape` = (B, H, n, d).  Returns (O bf16, LSE)."""
+    torch = _torch()
+    B, H, n, d = shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty((B, H, n, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q8.device) if lse is None else lse
+    for t, lay in ((q8, EXATTN_FP8_ROWS), (k8, EXATTN_FP8_ROWS), (v8t, EXATTN_FP8_V_TRANSPOSED)):
+        if t.dtype != torch.uint8 or not t.is_cuda or t.numel() < attn_fp8_bytes(B, H, n, d, lay):
+            raise ValueError("FP8 inputs must be uint8 GPU tensors of attn_fp8_bytes() bytes")
+    for t in (q_scale, k_scale, v_scale):
+        if t.dtype != torch.float32 or t.numel() != B * H or not t.is_cuda:
+            raise ValueError("scales must be float32 GPU tensors of B*H entries")
+    _call("attn_fwd_fp8", B, H, n, d, q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), q_scale.data_ptr(),
+          k_scale.data_ptr(), v_scale.data_ptr(), scale, int(bool(rotated)), out.data_ptr(), lse.data_ptr(),
+          (q8.device, _stream_ptr(q8, stream)))
+    return out, lse

@@ -403,3 +403,63 @@ int attn_bwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) forward and its quantiser
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t attn_fp8_bytes(int B, int H, int n, int d, int layout) {
+  if (check_problem(EXATTN_BF16, B, H, n, d, 1.0f, -1, H) != EXATTN_OK) return 0;
+  if (layout != EXATTN_FP8_ROWS && layout != EXATTN_FP8_V_TRANSPOSED) return 0;
+  const size_t cols = layout == EXATTN_FP8_ROWS ? (size_t)n : (size_t)exattn::fp8_padded_n(n);
+  return (size_t)B * H * cols * d;
+}
+
+int attn_quant_fp8(int B, int H, int n, int d, const void* X, const float* signs, int layout, void* X8,
+                   float* scale, void* stream) {
+  int st = check_problem(EXATTN_BF16, B, H, n, d, 1.0f, -1, H);
+  if (st != EXATTN_OK) return st;
+  if (d == 256) return EXATTN_EUNSUPPORTED;
+  if (layout != EXATTN_FP8_ROWS && layout != EXATTN_FP8_V_TRANSPOSED) return EXATTN_EINVAL;
+  const void* ptrs[] = {X, X8, scale};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return EXATTN_EINVAL;
+  if (signs != nullptr && ((uintptr_t)signs & 3u)) return EXATTN_EINVAL;
+  const size_t xb = (size_t)B * H * n * d * 2, qb = attn_fp8_bytes(B, H, n, d, layout);
+  const size_t sb = (size_t)B * H * sizeof(float);
+  const Span ins[] = {{X, xb}, {signs, signs ? (size_t)d * 4 : 0}};
+  const Span outs[] = {{X8, qb}, {scale, sb}};
+  for (const Span& o : outs)
+    for (const Span& in : ins)
+      if (in.n && overlaps(o.p, o.n, in.p, in.n)) return EXATTN_EINVAL;
+  if (overlaps(X8, qb, scale, sb)) return EXATTN_EINVAL;
+  exattn::Fp8QuantParams p{B, H, n, d, X, signs, X8, scale, layout == EXATTN_FP8_V_TRANSPOSED};
+  return from_hip(exattn::launch_quant_fp8(p, (hipStream_t)stream));
+}
+
+int attn_fwd_fp8(int B, int H, int n, int d, const void* Q8, const void* K8, const void* V8t, const float* q_scale,
+                 const float* k_scale, const float* v_scale, float scale, int rotated, void* O, float* LSE,
+                 void* stream) {
+  int st = check_problem(EXATTN_BF16, B, H, n, d, scale, -1, H);
+  if (st != EXATTN_OK) return st;
+  if (d != 128) return EXATTN_EUNSUPPORTED;
+  if (rotated != 0 && rotated != 1) return EXATTN_EINVAL;
+  const void* ptrs[] = {Q8, K8, V8t, O, LSE};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return EXATTN_EINVAL;
+  const void* sp[] = {q_scale, k_scale, v_scale};
+  for (const void* p : sp)
+    if (p == nullptr || ((uintptr_t)p & 3u)) return EXATTN_EINVAL;
+  const size_t qb = attn_fp8_bytes(B, H, n, d, EXATTN_FP8_ROWS);
+  const size_t vb = attn_fp8_bytes(B, H, n, d, EXATTN_FP8_V_TRANSPOSED);
+  const size_t ob = (size_t)B * H * n * d * 2, lb = (size_t)B * H * n * sizeof(float), sb = (size_t)B * H * 4;
+  const Span ins[] = {{Q8, qb}, {K8, qb}, {V8t, vb}, {q_scale, sb}, {k_scale, sb}, {v_scale, sb}};
+  for (const Span& in : ins)
+    if (overlaps(O, ob, in.p, in.n) || overlaps(LSE, lb, in.p, in.n)) return EXATTN_EINVAL;
+  if (overlaps(O, ob, LSE, lb)) return EXATTN_EINVAL;
+  exattn::Fp8FwdParams p{B, H, n, d, Q8, K8, V8t, q_scale, k_scale, v_scale, scale, rotated, O, LSE};
+  return from_hip(exattn::launch_fwd_fp8(p, (hipStream_t)stream));
+}
+
+}  // extern "C"
+

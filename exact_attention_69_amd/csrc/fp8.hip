@@ -1,0 +1,375 @@
+// FP8 (OCP E4M3) attention forward for gfx950, and the quantiser that feeds
+// it: FlashAttention-3's FP8 computation and "incoherent processing" (the
+// unite.ai page "Flash Attention: Revolucionando a Eficiencia dos Modelos
+// Transformer", section "FlashAttention-3", items 2 and 3).
+//
+// Quantiser (per (batch, head) and tensor):
+//   optional rotation x <- (x * signs) H, H the Sylvester Hadamard matrix
+//   (a fast Walsh-Hadamard transform of additions and subtractions, stages
+//   h = 1, 2, 4, ...), then scale = amax / 448 and code = e4m3(clamp(x *
+//   (448 / amax), +-448)).  Rotating Q and K by the same matrix multiplies
+//   Q K^T by d, which the forward divides out; it spreads outlier columns
+//   so the per-head scale is not set by a few large values.
+// Forward: S = scale / d_rot * s_q s_k * Q8 K8^T (32x32x64 FP8 MFMA, fp32
+// accumulation), online softmax in fp32 as in the bf16 kernel, P rounded
+// to E4M3 (values <= 2^8 by the lazy rescaling), O = s_v * P V8 / l in bf16.
+//
+// V is stored transposed, [B, H, d, n128] with n128 = n rounded up to 128,
+// and within every 64-key group the keys are permuted so that the 32 keys
+// a lane holds in its score accumulator (rows 8a + 4h + c, a, c = 0..3, of
+// each of two 32-key blocks) form one contiguous 32-byte MFMA operand:
+//   key 32*kb + 8*a + 4*h + c  ->  column 32*h + 16*kb + 4*a + c.
+// Columns at or beyond n hold zeros.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace exattn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // cbsz = blgp = 0: both operands E4M3; unit block scales (exponent 127)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four E4M3 codes (ties to even) packed into one dword, a in byte 0.
+__device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Column of key `k` (within its 64-key group) in the transposed V layout.
+__host__ __device__ inline int vt_column(int k) {
+  const int g = k >> 6, r = k & 63;
+  const int kb = r >> 5, a = (r >> 3) & 3, h = (r >> 2) & 1, c = r & 3;
+  return (g << 6) + 32 * h + 16 * kb + 4 * a + c;
+}
+
+// ---------------------------------------------------------------------------
+// Quantiser
+// ---------------------------------------------------------------------------
+// One wave per row, EPL = d / 64 elements per lane: element i = lane + 64*e.
+template <int D>
+__device__ __forceinline__ void load_rotated_row(const __bf16* __restrict__ row, const float* __restrict__ signs,
+                                                 int lane, float (&x)[D / 64]) {
+  constexpr int EPL = D / 64;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] = (float)row[lane + 64 * e];
+  if (signs == nullptr) return;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] *= signs[lane + 64 * e];
+  // stages h = 1 .. 32 across lanes, then h = 64 (and 128) within the lane
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float b = __shfl_xor(x[e], h, 64);
+      x[e] = (lane & h) ? b - x[e] : x[e] + b;
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < EPL; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if ((e & h) == 0) {
+        const float a = x[e], b = x[e + h];
+        x[e] = a + b;
+        x[e + h] = a - b;
+      }
+}
+
+__global__ __launch_bounds__(256) void quant_clear_kernel(uint32_t* __restrict__ amax_bits, int heads) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < heads) amax_bits[i] = 0u;
+}
+
+// amax of every head: |x| as uint bits (monotonic for non-negative floats).
+template <int D>
+__global__ __launch_bounds__(256) void quant_amax_kernel(const __bf16* __restrict__ X, const float* __restrict__ signs,
+                                                        uint32_t* __restrict__ amax_bits, int n, long rows) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float x[D / 64];
+  load_rotated_row<D>(X + row * D, signs, lane, x);
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+  if (lane == 0) atomicMax(&amax_bits[row / n], __float_as_uint(m));
+}
+
+// codes; `transposed`: write the V layout described at the top; rows
+// n .. n128-1 of a head write zero columns there.
+template <int D>
+__global__ __launch_bounds__(256) void quant_codes_kernel(const __bf16* __restrict__ X,
+                                                         const float* __restrict__ signs,
+                                                         const uint32_t* __restrict__ amax_bits,
+                                                         uint8_t* __restrict__ X8, int n, int n128, long heads,
+                                                         int transposed) {
+  const int lane = threadIdx.x & 63;
+  const long prow = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // row in [heads * rows_per_head)
+  const int rows_per_head = transposed ? n128 : n;
+  if (prow >= heads * rows_per_head) return;
+  const long head = prow / rows_per_head;
+  const int r = (int)(prow - head * rows_per_head);
+  float x[D / 64];
+  if (r < n) {
+    load_rotated_row<D>(X + (head * n + r) * D, signs, lane, x);
+  } else {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) x[e] = 0.0f;
+  }
+  const float amax = __uint_as_float(amax_bits[head]);
+  const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) {
+    const float q = fminf(fmaxf(x[e] * inv, -kE4M3Max), kE4M3Max);
+    const uint8_t code = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xff);
+    const int i = lane + 64 * e;
+    if (transposed)
+      X8[(head * D + i) * n128 + vt_column(r)] = code;
+    else
+      X8[(head * n + r) * D + i] = code;
+  }
+}
+
+__global__ __launch_bounds__(256) void quant_scale_kernel(float* __restrict__ scale, int heads) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= heads) return;
+  const float amax = scale[i];  // the amax bits left by quant_amax_kernel
+  scale[i] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+constexpr int kF8NW = 8;    // waves (256 query rows per workgroup)
+constexpr int kF8BC = 128;  // keys per tile
+
+// Direct global -> LDS copy of ROWS rows of 128 bytes (global row stride
+// `stride` bytes) into the XOR-swizzled layout of 16-byte chunks used by
+// the bf16 kernels for 128-byte rows.  Rows at or beyond `valid` re-read
+// row valid-1.
+template <int ROWS, int NT>
+__device__ __forceinline__ void tile8_issue(const uint8_t* __restrict__ src, long stride, int valid, uint8_t* lds,
+                                            int tid) {
+  constexpr int CPR = 8;
+  constexpr int IT = ROWS * CPR / NT;
+  static_assert((ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int slot0 = it * NT + wave * 64;
+    const int p = slot0 + lane;
+    const int row = p / CPR;
+    const int c = swz_chunk<64>(row, p % CPR);
+    const int srow = row < valid ? row : valid - 1;
+    lds_dma16(src + (long)srow * stride + 16 * c, lds + 16 * slot0);
+  }
+}
+
+// 32 contiguous bytes [32*j, 32*j + 32) of a 128-byte row of a swizzled tile.
+__device__ __forceinline__ i32x8 lds_frag32(const uint8_t* tile, int row, int j) {
+  const u32x4 a = *(const u32x4*)(tile + row * 128 + 16 * swz_chunk<64>(row, 2 * j));
+  const u32x4 b = *(const u32x4*)(tile + row * 128 + 16 * swz_chunk<64>(row, 2 * j + 1));
+  i32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8t,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n128, int n_qblocks, int total_blocks,
+    float scale_log2_base) {
+  static_assert(D == 128, "the FP8 forward is built for d = 128");
+  constexpr int NW = kF8NW, BC = kF8BC, BR = 32 * NW, NT = NW * 64;
+  constexpr int NKB = BC / 32;  // 32-key blocks per tile
+  constexpr int NDS = D / 64;   // 64-wide d steps of S
+  constexpr int NDB = D / 32;   // 32-wide d blocks of O
+  constexpr int NPS = BC / 64;  // 64-key steps of P V
+
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][D * BC];
+
+  const int bid = xcd_remap(blockIdx.x, total_blocks);
+  const int head = bid / n_qblocks;
+  const int qb = bid - head * n_qblocks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+
+  const uint8_t* K = K8 + (size_t)head * n * D;
+  const uint8_t* Vt = V8t + (size_t)head * D * n128;
+  const int my_row = qb * BR + wave * 32 + l32;
+  const float scale_log2 = scale_log2_base * q_scale[head] * k_scale[head];
+
+  // Q^T operand in registers: lane holds Q8[my_row][64*ds + 32*hi .. +32]
+  i32x8 qreg[NDS];
+  {
+    const bool ok = my_row < n;
+    const i32x8* src = (const i32x8*)(Q8 + ((size_t)head * n + (ok ? my_row : 0)) * D + 32 * hi);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      qreg[ds] = ok ? src[2 * ds] : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  auto issue_k = [&](int t, uint8_t* buf) { tile8_issue<BC, NT>(K + (size_t)t * BC * D, D, n - t * BC, buf, tid); };
+  auto issue_v = [&](int t, uint8_t* buf) { tile8_issue<D, NT>(Vt + (size_t)t * BC, n128, D, buf, tid); };
+  auto compute_s_block = [&](const uint8_t* Ks, int kb, f32x16 (&s)[NKB]) {
+    s[kb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma_f8(lds_frag32(Ks, kb * 32 + l32, 2 * ds + hi), qreg[ds], s[kb]);
+  };
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+  float m_run = kNegInf, l_part = 0.0f;
+
+  const int n_tiles = (n + BC - 1) / BC;
+  if (n_tiles > 0) {
+    issue_k(0, kbuf[0]);
+    issue_v(0, vbuf[0]);
+    if (n_tiles > 1) issue_k(1, kbuf[1]);
+  }
+  wait_all_and_barrier();
+  f32x16 s_cur[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) compute_s_block(kbuf[0], kb, s_cur);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    if (j + 1 < n_tiles) issue_v(j + 1, vbuf[(j + 1) & 1]);
+    if (j + 2 < n_tiles) issue_k(j + 2, kbuf[j & 1]);
+    const int kbase = j * BC;
+    if (kbase + BC > n) {  // key tail
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + kb * 32 + acc_row(r, lane);
+          s_cur[kb][r] = key < n ? s_cur[kb][r] : kNegInf;
+        }
+    }
+    // running max and (rare) rescale, as in the bf16 kernel
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
+    mx = pair_max(mx);
+    const float mx2 = mx * scale_log2;
+    const bool grow = mx2 > m_run + 8.0f || (m_run == kNegInf && mx2 != kNegInf);
+    if (__any(grow)) {
+      const float m_new = grow ? mx2 : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float msub = m_run == kNegInf ? 0.0f : m_run;
+
+    // P in E4M3, packed in the transposed V layout's key order: for P V step
+    // ps (keys 64*ps ..), byte 16*kb' + r of the lane's operand is P of
+    // accumulator element r of key block 2*ps + kb'.  Each converted block's
+    // fp32 registers then receive that block of the next tile's S.
+    i32x8 pb[NPS];
+    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s_cur[kb][r] = fast_exp2(__builtin_fmaf(s_cur[kb][r], scale_log2, -msub));
+        lsum[r & 3] += s_cur[kb][r];
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        pb[kb >> 1][4 * (kb & 1) + w] =
+            pack_e4m3x4(s_cur[kb][4 * w], s_cur[kb][4 * w + 1], s_cur[kb][4 * w + 2], s_cur[kb][4 * w + 3]);
+      compute_s_block(kbuf[(j + 1) & 1], kb, s_cur);
+    }
+    l_part += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+
+    // O^T += V^T P^T: A = V^T rows (d) with 32 keys per lane, B = P^T.
+    const uint8_t* Vs = vbuf[j & 1];
+#pragma unroll
+    for (int ps = 0; ps < NPS; ++ps)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] = mfma_f8(lds_frag32(Vs, db * 32 + l32, 2 * ps + hi), pb[ps], o[db]);
+
+    wait_all_and_barrier();
+  }
+
+  const float l_tot = pair_sum(l_part);
+  if (my_row < n) {
+    const float inv = v_scale[head] / l_tot;
+    __bf16* Orow = Og + ((size_t)head * n + my_row) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = db * 32 + 8 * g + 4 * hi;
+        u32x2 w;
+        w[0] = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *(u32x2*)(Orow + dd) = w;
+      }
+    if (hi == 0) LSEg[(size_t)head * n + my_row] = kLn2 * (m_run + fast_log2(l_tot));
+  }
+}
+
+}  // namespace
+
+int fp8_padded_n(int n) { return (n + kF8BC - 1) / kF8BC * kF8BC; }
+
+hipError_t launch_quant_fp8(const Fp8QuantParams& p, hipStream_t stream) {
+  const long heads = (long)p.B * p.H;
+  const long rows = heads * p.n;
+  const int n128 = fp8_padded_n(p.n);
+  uint32_t* amax = (uint32_t*)p.scale;
+  hipLaunchKernelGGL(quant_clear_kernel, dim3((unsigned)((heads + 255) / 256)), dim3(256), 0, stream, amax,
+                     (int)heads);
+  const long code_rows = heads * (p.transposed ? n128 : p.n);
+  switch (p.d) {
+    case 64:
+      hipLaunchKernelGGL((quant_amax_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                         (const __bf16*)p.x, p.signs, amax, p.n, rows);
+      hipLaunchKernelGGL((quant_codes_kernel<64>), dim3((unsigned)((code_rows + 3) / 4)), dim3(256), 0, stream,
+                         (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, heads, p.transposed);
+      break;
+    case 128:
+      hipLaunchKernelGGL((quant_amax_kernel<128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                         (const __bf16*)p.x, p.signs, amax, p.n, rows);
+      hipLaunchKernelGGL((quant_codes_kernel<128>), dim3((unsigned)((code_rows + 3) / 4)), dim3(256), 0, stream,
+                         (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, heads, p.transposed);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(quant_scale_kernel, dim3((unsigned)((heads + 255) / 256)), dim3(256), 0, stream, p.scale,
+                     (int)heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
+  if (p.d != 128) return hipErrorInvalidValue;
+  constexpr int BR = 32 * kF8NW;
+  const int nqb = (p.n + BR - 1) / BR;
+  const long total = (long)nqb * p.B * p.H;
+  if (total > 0x7fffffffL) return hipErrorInvalidValue;
+  const float scale_log2 = p.scale / (p.rotated ? (float)p.d : 1.0f) * kLog2e;
+  hipLaunchKernelGGL((fwd_fp8_kernel<128>), dim3((unsigned)total), dim3(kF8NW * 64), 0, stream,
+                     (const uint8_t*)p.q8, (const uint8_t*)p.k8, (const uint8_t*)p.v8t, p.q_scale, p.k_scale,
+                     p.v_scale, (__bf16*)p.o, p.lse, p.n, fp8_padded_n(p.n), nqb, (int)total, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace exattn

@@ -55,6 +55,32 @@ enum BwdStage : unsigned { kStageRowdot = 1, kStageKV = 2, kStageQ = 4, kStageAl
 hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdParams& p, unsigned stages, hipStream_t stream);
 
+// FP8: per-head quantiser (optional Hadamard rotation) and the forward.
+struct Fp8QuantParams {
+  int B, H, n, d;
+  const void* x;       // bf16 [B, H, n, d]
+  const float* signs;  // d signs (+-1) of the rotation, or nullptr
+  void* x8;            // E4M3 codes: [B, H, n, d], or the transposed V layout
+  float* scale;        // [B, H]
+  int transposed;
+};
+struct Fp8FwdParams {
+  int B, H, n, d;
+  const void* q8;
+  const void* k8;
+  const void* v8t;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  float scale;
+  int rotated;
+  void* o;
+  float* lse;
+};
+int fp8_padded_n(int n);
+hipError_t launch_quant_fp8(const Fp8QuantParams& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
+
 // Band of the sliding window, used to skip tiles (host and device).
 // Keys [lo, hi) that any row in [r0, r1) may attend to.
 __host__ __device__ inline void band_keys(int r0, int r1, int n, int window, int* lo, int* hi) {

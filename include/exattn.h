@@ -276,6 +276,53 @@ int attn_bwd_pattern(int dtype, int B, int H, int n, int d,
                      void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/*
+ * FP8 forward (FlashAttention-3's FP8 support and "incoherent processing",
+ * the unite.ai page's section "FlashAttention-3", items 2 and 3).  Format:
+ * OCP E4M3 (largest finite 448), one scale per (batch, head) and tensor.
+ *
+ * attn_quant_fp8 quantises a bf16 [B, H, n, d] tensor (d = 64 or 128): with
+ * `signs` (a device array of d floats, each +1 or -1) every row is first
+ * multiplied by the signs and transformed by the Sylvester Hadamard matrix
+ * H of order d (a fast Walsh-Hadamard transform; H H^T = d I); then
+ * scale[b, h] = amax / 448 over the head (1 for an all-zero head) and each
+ * code is E4M3(clamp(x * 448 / amax, -448, 448)), rounded to nearest even.
+ * `layout` EXATTN_FP8_ROWS writes [B, H, n, d] (for Q and K);
+ * EXATTN_FP8_V_TRANSPOSED writes V's layout for attn_fwd_fp8: [B, H, d, n128]
+ * with n128 = n rounded up to a multiple of 128, and within every 64-key
+ * group key 32*kb + 8*a + 4*h + c (kb, h in {0,1}; a, c in {0..3}) stored
+ * at column 32*h + 16*kb + 4*a + c (the order in which the forward's score
+ * accumulators hold the keys); columns at or beyond n are zero.
+ * attn_fp8_bytes returns the byte size of either layout (0 if invalid).
+ *
+ * attn_fwd_fp8 (d = 128): O = softmax(S) V with
+ *   S = scale / (rotated ? d : 1) * q_scale * k_scale * Q8 K8^T,
+ *   V = v_scale * V8,
+ * both products on the FP8 matrix cores with fp32 accumulation; the
+ * probabilities are rounded to E4M3 before the P V product.  Q and K must
+ * have been quantised with the same signs (rotated = 1) or both without
+ * (rotated = 0); V without.  O is bf16 [B, H, n, d], LSE fp32 [B, H, n].
+ * Errors: EXATTN_EINVAL for null or misaligned pointers (16 bytes; 4 for
+ * the scale and sign arrays), a bad layout or rotated flag, or overlapping
+ * outputs; EXATTN_EUNSUPPORTED for d = 256 (quantiser) or d != 128
+ * (forward).
+ */
+typedef enum { EXATTN_FP8_ROWS = 0, EXATTN_FP8_V_TRANSPOSED = 1 } exattn_fp8_layout;
+
+size_t attn_fp8_bytes(int B, int H, int n, int d, int layout);
+
+int attn_quant_fp8(int B, int H, int n, int d,
+                   const void *X, const float *signs, int layout,
+                   void *X8, float *scale,
+                   void *stream);
+
+int attn_fwd_fp8(int B, int H, int n, int d,
+                 const void *Q8, const void *K8, const void *V8t,
+                 const float *q_scale, const float *k_scale, const float *v_scale,
+                 float scale, int rotated,
+                 void *O, float *LSE,
+                 void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *exattn_status_string(int status);
 

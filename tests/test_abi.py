@@ -38,8 +38,9 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dkdv_gqa", "attn_bwd_dq",
                                     "attn_bwd_dq_gqa", "attn_bwd_gqa", "attn_bwd_pattern", "attn_bwd_rowdot",
-                                    "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_gqa", "attn_fwd_pattern",
-                                    "attn_pattern_workspace_bytes", "exattn_status_string"]
+                                    "attn_bwd_workspace_bytes", "attn_fp8_bytes", "attn_fwd", "attn_fwd_fp8",
+                                    "attn_fwd_gqa", "attn_fwd_pattern", "attn_pattern_workspace_bytes",
+                                    "attn_quant_fp8", "exattn_status_string"]
 
 
 def test_binding_wraps_every_declared_symbol():
@@ -214,6 +215,30 @@ def test_pattern_entry_points_reject_bad_arguments(lib):
     assert bw(None) == EINVAL
     assert bw(good, wsb=need - 1) == EWORKSPACE
     assert bw(_pat(window=-5)) == EINVAL
+
+
+def test_fp8_entry_points_reject_bad_arguments(lib):
+    n, d = 300, 128
+    assert lib.attn_fp8_bytes(1, 2, n, d, 0) == 2 * n * d
+    assert lib.attn_fp8_bytes(1, 2, n, d, 1) == 2 * 384 * d  # n rounded up to 128
+    assert lib.attn_fp8_bytes(1, 2, n, d, 2) == 0
+    x, signs, x8, sc = ptrs(4)
+    q = lambda **kw: lib.attn_quant_fp8(kw.get("B", 1), 2, n, kw.get("d", d), kw.get("x", x), kw.get("signs", signs),
+                                        kw.get("layout", 0), kw.get("x8", x8), kw.get("sc", sc), None)
+    assert q(B=0) == EINVAL
+    assert q(d=256) == EUNSUPPORTED
+    assert q(d=80) == EUNSUPPORTED
+    assert q(layout=5) == EINVAL
+    assert q(x=None) == EINVAL
+    assert q(signs=ctypes.c_void_p(signs.value + 2)) == EINVAL
+    assert q(x8=ctypes.c_void_p(x.value + 64)) == EINVAL  # codes overlap the input
+    q8, k8, v8, qs, ks, vs, o, lse = ptrs(8)
+    f = lambda **kw: lib.attn_fwd_fp8(1, 2, n, kw.get("d", d), q8, k8, kw.get("v8", v8), qs, ks, vs, 0.1,
+                                      kw.get("rot", 0), kw.get("o", o), lse, None)
+    assert f(d=64) == EUNSUPPORTED
+    assert f(rot=2) == EINVAL
+    assert f(v8=None) == EINVAL
+    assert f(o=ctypes.c_void_p(k8.value + 16)) == EINVAL
 
 
 def test_binding_rejects_host_tensors():

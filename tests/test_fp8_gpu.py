@@ -1,0 +1,140 @@
+"""GPU parity of the FP8 path (E4M3 quantiser with the optional Hadamard
+rotation, and the FP8 forward) against the CPU oracle, through the C ABI.
+
+The quantiser's codes and scales are compared bit for bit: both sides take
+every rounding decision in fp32 (the rotation is additions and subtractions
+in the same butterfly order).  The forward is compared with the oracle's
+fp64 attention of the oracle's own codes; the difference is the GPU's
+rounding of P to E4M3 before the P V product, bounded below.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import make_case, to_device
+from workloads import VARIANTS, draw_inputs, draw_signs
+
+pytestmark = pytest.mark.gpu
+
+# The GPU rounds P to E4M3 before the P V product; everything else matches
+# the oracle's arithmetic up to fp32 accumulation order.  E4M3 keeps 3
+# mantissa bits: a rounding error of at most 2**-4 of each probability, and
+# an rms relative error of (2**-3 / sqrt(12)) * E[2**e / x] ~ 0.036 * 0.72
+# ~ 2.6% for values spread over a binade.  O is a normalised combination of
+# the rows of V, so
+#   worst case: |O_gpu - O| <= 2**-4 * max|V| (every weight off by 2**-4);
+#   rms:        ||O_gpu - O||_F / ||O||_F ~ 2.6%, gated at 4e-2.
+# LSE comes from the fp32 scores (no P rounding): 1e-4 absolute.
+FP8_O_FRO_REL = 4e-2
+FP8_O_MAX_OF_V = 2.0 ** -4
+FP8_LSE_ABS = 1e-4
+
+
+def e4m3_values():
+    """Value of each byte 0..255 from the format's bit layout (NaN codes nan)."""
+    v = np.empty(256)
+    for b in range(256):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        x = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        v[b] = np.nan if (e == 15 and m == 7) else (-x if s else x)
+    return v
+
+
+def vt_column(k):
+    g, r = k // 64, k % 64
+    kb, a, h, c = r // 32, (r // 8) % 4, (r // 4) % 2, r % 4
+    return 64 * g + 32 * h + 16 * kb + 4 * a + c
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quantiser_codes_and_scales_are_exact(d, rotate):
+    import torch
+    import exact_attention_69_amd as ea
+    wl = make_case(1, 2, 300, d, "bf16", seed=13 + d)
+    x = draw_inputs(wl, ("q",))["q"]
+    x[0, 1, 7, 3] = 40.0  # an outlier in one head
+    signs = draw_signs(wl) if rotate else None
+    t = to_device({"x": x}, "bf16")["x"]
+    sg = torch.from_numpy(signs).to("cuda") if rotate else None
+    codes, scale = ea.attn_quant_fp8(t, sg, ea.EXATTN_FP8_ROWS)
+    torch.cuda.synchronize()
+    vals = e4m3_values()[codes.cpu().numpy()].reshape(x.shape)
+    sc = scale.cpu().numpy()
+    for h in range(2):
+        c_ref, s_ref = oracle.quantize_head(x[0, h], signs)
+        np.testing.assert_array_equal(vals[0, h], c_ref)
+        assert sc[0, h] == s_ref  # fp32 bit for bit
+    if d == 128 or not rotate:  # the transposed V layout (no rotation for V)
+        codes_t, scale_t = ea.attn_quant_fp8(t, None, ea.EXATTN_FP8_V_TRANSPOSED)
+        torch.cuda.synchronize()
+        n, n128 = 300, 384
+        vt = e4m3_values()[codes_t.cpu().numpy()].reshape(1, 2, d, n128)
+        cols = np.array([vt_column(k) for k in range(n128)])
+        for h in range(2):
+            c_ref, s_ref = oracle.quantize_head(x[0, h])
+            np.testing.assert_array_equal(vt[0, h][:, cols[:n]].T, c_ref)
+            assert np.all(vt[0, h][:, cols[n:]] == 0.0)
+            assert scale_t.cpu().numpy()[0, h] == s_ref
+
+
+def run_fp8(wl, x, signs):
+    import torch
+    import exact_attention_69_amd as ea
+    t = to_device(x, "bf16")
+    sg = torch.from_numpy(signs).to("cuda") if signs is not None else None
+    q8, qs = ea.attn_quant_fp8(t["q"], sg, ea.EXATTN_FP8_ROWS)
+    k8, ks = ea.attn_quant_fp8(t["k"], sg, ea.EXATTN_FP8_ROWS)
+    v8, vs = ea.attn_quant_fp8(t["v"], None, ea.EXATTN_FP8_V_TRANSPOSED)
+    o, lse = ea.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, t["q"].shape, wl.scale, rotated=signs is not None)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def check_fp8(o, lse, O, L, vmax, label):
+    fro = float(np.linalg.norm(o - O) / np.linalg.norm(O))
+    emax = float(np.max(np.abs(o - O)) / vmax)
+    el = float(np.max(np.abs(lse - L)))
+    print(f"[fp8] {label}: o_fro={fro:.2e} o_max/max|V|={emax:.2e} lse={el:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert fro <= FP8_O_FRO_REL, f"{label}: O Frobenius error {fro:.3e}"
+    assert emax <= FP8_O_MAX_OF_V, f"{label}: O max error {emax:.3e} of max|V|"
+    assert el <= FP8_LSE_ABS, f"{label}: LSE error {el:.3e}"
+
+
+def vmax_of(v):
+    """max|V| after quantisation (per head scale times 448 bounds it)."""
+    return max(float(np.max(np.abs(oracle.quantize_head(v[idx])[0]))) * float(oracle.quantize_head(v[idx])[1])
+               for idx in np.ndindex(*v.shape[:-2]))
+
+
+@pytest.mark.parametrize("n", [1, 100, 300, 1000])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_fp8_forward_matches_oracle(n, rotate):
+    wl = make_case(1, 2, n, 128, "bf16", seed=29 + n)
+    x = draw_inputs(wl, ("q", "k", "v"))
+    signs = draw_signs(wl) if rotate else None
+    o, lse = run_fp8(wl, x, signs)
+    O, L = oracle.attention_forward_fp8(x["q"], x["k"], x["v"], wl.scale, signs)
+    check_fp8(o, lse, O, L, vmax_of(x["v"]), f"n{n}_rot{int(rotate)}")
+
+
+FP8_VARIANTS = [w for w in VARIANTS if w.fp8]
+
+
+@pytest.mark.parametrize("wl", FP8_VARIANTS, ids=[w.name for w in FP8_VARIANTS])
+def test_fp8_full_size(wl):
+    print(f"[fp8-full] {wl.name}", flush=True)
+    x = draw_inputs(wl, ("q", "k", "v"))
+    signs = draw_signs(wl) if wl.rotate else None
+    o, lse = run_fp8(wl, x, signs)
+    heads = [(0, 0), (wl.B - 1, wl.H - 1)]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        O, L = oracle.attention_forward_fp8(x["q"][sl], x["k"][sl], x["v"][sl], wl.scale, signs)
+        check_fp8(o[sl], lse[sl], O, L, vmax_of(x["v"][sl]), f"{wl.name} head {(b, h)}")
+    sys.stdout.flush()

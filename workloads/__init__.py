@@ -24,6 +24,8 @@ on its own without drawing the whole problem):
   rows and columns, and, in every other block row, ``random`` further blocks
   drawn without replacement from the unset ones (``SeedSequence([seed, 200,
   row])``).  The same arrays go to the GPU and to the oracle.
+* FP8 rotation signs: ``+-1`` with equal probability from
+  ``SeedSequence([seed, 300])``.
 """
 
 from dataclasses import dataclass, field
@@ -40,6 +42,7 @@ __all__ = [
     "draw_inputs",
     "pair_count",
     "draw_pattern",
+    "draw_signs",
     "pattern_pair_count",
     "LAYOUT_BLOCK",
 ]
@@ -64,6 +67,8 @@ class Workload:
     kv_heads: int = 0  # 0: one key/value head per query head
     n_global: int = 0  # sparse pattern: number of global tokens
     bigbird: tuple = ()  # sparse pattern: (local, global, random) blocks of 64
+    fp8: bool = False  # FP8 forward (E4M3 inputs quantised per head)
+    rotate: bool = False  # FP8: Hadamard rotation of Q and K with drawn signs
     note: str = field(default="", compare=False)
 
     @property
@@ -110,7 +115,16 @@ VARIANTS = [
              n_global=16, note="Longformer: window |i-j|<=256 plus 16 global tokens"),
     Workload("bf16_b1h16_n16384_d128_bigbird_b64", 1, 16, 16384, 128, "bf16", seed=69008, bigbird=(3, 2, 3),
              note="BigBird: 64-token blocks, 3 local, 2 global, 3 random per block row"),
+    Workload("fp8_b2h32_n8192_d128_rot", 2, 32, 8192, 128, "bf16", seed=69009, fp8=True, rotate=True,
+             note="FP8 forward: E4M3 inputs with the Hadamard rotation of Q and K"),
 ]
+
+
+def draw_signs(wl, d=None):
+    """The +-1 signs of the FP8 rotation (float32, d entries)."""
+    d = wl.d if d is None else d
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 300])))
+    return np.where(g.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
 
 LAYOUT_BLOCK = 64
 
