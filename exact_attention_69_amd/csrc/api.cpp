@@ -239,14 +239,22 @@ namespace {
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Workspace layout for a pattern problem: [global bitmap][forward lists]
-// [key-side lists][query-side lists][D][LSE*log2(e)], each region 256-byte
-// aligned.  Lists hold, per workgroup row of the kernel's grid, one entry per
-// tile of the other side (the most a workgroup can visit) and a count.
+// Workspace layout for a pattern problem: [global bitmap][full-row bitmap]
+// [full-key bitmap][layout flags][full-row list][full-key list][split info]
+// [forward lists][key-side lists][query-side lists][partial results]
+// [D][LSE*log2(e)], each region 256-byte aligned.  Lists hold, per workgroup
+// row of the kernel's grid, one entry per tile of the other side (the most a
+// workgroup can visit) and a count.  The partial results of the full
+// positions take full_part_rows(n) slots per head of 2d floats (forward: d
+// for O, then one log-sum-exp per slot after all the O slots).
 struct PatternLayout {
-  size_t bitmap, fwd, kv, q, rows, total;
+  size_t bitmap, flags, idx, info, fwd, kv, q, part, rows, total;
   int fwd_R, fwd_T, fwd_NW, kv_R, kv_T, kv_NW, q_R, q_T, q_NW;
   int fwd_blocks, fwd_tiles, kv_blocks, kv_tiles, q_blocks, q_tiles;
+  size_t part_floats;  // floats of the partial-result region
+  // offsets from the start of the workspace
+  size_t off_gbits, off_rowfull, off_colfull, off_flags, off_rowidx, off_colidx, off_info, off_fwd, off_kv, off_q,
+      off_part, off_rows;
 };
 
 PatternLayout pattern_layout(int B, int H, int n, int d) {
@@ -260,12 +268,30 @@ PatternLayout pattern_layout(int B, int H, int n, int d) {
   L.kv_tiles = (n + L.kv_T - 1) / L.kv_T;
   L.q_blocks = (n + L.q_R - 1) / L.q_R;
   L.q_tiles = (n + L.q_T - 1) / L.q_T;
+  const size_t nb = (size_t)(n + exattn::kLayoutBlock - 1) / exattn::kLayoutBlock;
   L.bitmap = align256((size_t)exattn::bitmap_words(n) * 4);
+  L.flags = align256(2 * nb * 4);
+  L.idx = align256((size_t)n * 4);
+  L.info = align256(3 * exattn::kFullInfoInts * 4);
   L.fwd = align256((size_t)L.fwd_blocks * (L.fwd_tiles + 1) * 4);
   L.kv = align256((size_t)L.kv_blocks * (L.kv_tiles + 1) * 4);
   L.q = align256((size_t)L.q_blocks * (L.q_tiles + 1) * 4);
+  L.part_floats = (size_t)B * H * exattn::full_part_rows(n) * 2 * d;
+  L.part = align256(L.part_floats * 4);
   L.rows = 2 * ws_region_bytes(B, H, n);
-  L.total = L.bitmap + L.fwd + L.kv + L.q + L.rows;
+  L.off_gbits = 0;
+  L.off_rowfull = L.off_gbits + L.bitmap;
+  L.off_colfull = L.off_rowfull + L.bitmap;
+  L.off_flags = L.off_colfull + L.bitmap;
+  L.off_rowidx = L.off_flags + L.flags;
+  L.off_colidx = L.off_rowidx + L.idx;
+  L.off_info = L.off_colidx + L.idx;
+  L.off_fwd = L.off_info + L.info;
+  L.off_kv = L.off_fwd + L.fwd;
+  L.off_q = L.off_kv + L.kv;
+  L.off_part = L.off_q + L.q;
+  L.off_rows = L.off_part + L.part;
+  L.total = L.off_rows + L.rows;
   return L;
 }
 
@@ -286,7 +312,8 @@ size_t layout_bytes(const exattn_pattern* pat, int n) {
   return nb * nb;
 }
 
-exattn::PlanInput plan_input(const exattn_pattern* pat, int n, void* workspace) {
+exattn::PlanInput plan_input(const exattn_pattern* pat, int n, void* workspace, const PatternLayout& L) {
+  char* ws = (char*)workspace;
   exattn::PlanInput in{};
   in.n = n;
   in.window = pat->window;
@@ -294,8 +321,18 @@ exattn::PlanInput plan_input(const exattn_pattern* pat, int n, void* workspace) 
   in.global_idx = pat->global_idx;
   in.layout = pat->layout_block ? pat->layout : nullptr;
   in.layout_n = (n + exattn::kLayoutBlock - 1) / exattn::kLayoutBlock;
-  in.gbits = (uint32_t*)workspace;
+  in.gbits = (uint32_t*)(ws + L.off_gbits);
+  in.row_full = (uint32_t*)(ws + L.off_rowfull);
+  in.col_full = (uint32_t*)(ws + L.off_colfull);
+  in.layout_flags = (int*)(ws + L.off_flags);
+  in.row_idx = (int*)(ws + L.off_rowidx);
+  in.col_idx = (int*)(ws + L.off_colidx);
   return in;
+}
+
+// Split info of consumer kernel `k` (0: forward, 1: key side, 2: query side).
+int* full_info(void* workspace, const PatternLayout& L, int k) {
+  return (int*)((char*)workspace + L.off_info) + k * exattn::kFullInfoInts;
 }
 
 // Builds one list in the region at `base`; returns the run-time descriptor.
@@ -307,11 +344,12 @@ hipError_t build_list(const exattn::PlanInput& in, char* base, int R, int T, int
   pl.NW = NW;
   pl.transposed = transposed;
   pl.tail_partial = tail_partial;
+  pl.own_full = transposed ? in.col_full : in.row_full;
   pl.count = (int*)base;
   pl.list = (int*)base + blocks;
   pl.stride = tiles;
   pl.nblocks = blocks;
-  *dev = exattn::PatternDev{in.window, in.gbits, pl.list, pl.count, tiles};
+  *dev = exattn::PatternDev{in.window, in.gbits, pl.own_full, pl.list, pl.count, tiles};
   return exattn::launch_pattern_list(in, pl, s);
 }
 
@@ -350,11 +388,14 @@ int attn_fwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const
   }
 
   hipStream_t s = (hipStream_t)stream;
-  const exattn::PlanInput in = plan_input(pattern, n, workspace);
-  hipError_t e = exattn::launch_pattern_bitmap(in, s);
+  const exattn::PlanInput in = plan_input(pattern, n, workspace, L);
+  const exattn::FullSplit split{L.fwd_tiles, false, full_info(workspace, L, 0)};
+  hipError_t e = exattn::launch_pattern_bitmap(in, &split, 1, s);
   exattn::FwdParams p{Q, K, V, O, LSE, B, H, n, d, scale, -1, 1};
+  float* part = (float*)((char*)workspace + L.off_part);
+  p.full = exattn::FullDev{in.row_idx, split.info, part, part + (size_t)B * H * exattn::full_part_rows(n) * d};
   if (e == hipSuccess)
-    e = build_list(in, (char*)workspace + L.bitmap, L.fwd_R, L.fwd_T, L.fwd_NW, L.fwd_blocks, L.fwd_tiles, false,
+    e = build_list(in, (char*)workspace + L.off_fwd, L.fwd_R, L.fwd_T, L.fwd_NW, L.fwd_blocks, L.fwd_tiles, false,
                    true, &p.pattern, s);
   if (e == hipSuccess) e = exattn::launch_fwd_bf16(p, s);
   return from_hip(e);
@@ -386,17 +427,20 @@ int attn_bwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const
   }
 
   hipStream_t s = (hipStream_t)stream;
-  const exattn::PlanInput in = plan_input(pattern, n, workspace);
+  const exattn::PlanInput in = plan_input(pattern, n, workspace, L);
   char* base = (char*)workspace;
-  void* rows = base + L.bitmap + L.fwd + L.kv + L.q;
-  exattn::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, dQ, dK, dV, rows, B, H, n, d, scale, -1, 1);
-  hipError_t e = exattn::launch_pattern_bitmap(in, s);
+  exattn::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, dQ, dK, dV, base + L.off_rows, B, H, n, d, scale, -1, 1);
+  const exattn::FullSplit splits[2] = {{L.kv_tiles, true, full_info(workspace, L, 1)},
+                                       {L.q_tiles, false, full_info(workspace, L, 2)}};
+  float* part = (float*)(base + L.off_part);
+  p.full_kv = exattn::FullDev{in.col_idx, splits[0].info, part, nullptr};
+  p.full_q = exattn::FullDev{in.row_idx, splits[1].info, part, nullptr};
+  hipError_t e = exattn::launch_pattern_bitmap(in, splits, 2, s);
   if (e == hipSuccess)
-    e = build_list(in, base + L.bitmap + L.fwd, L.kv_R, L.kv_T, L.kv_NW, L.kv_blocks, L.kv_tiles, true, false,
+    e = build_list(in, base + L.off_kv, L.kv_R, L.kv_T, L.kv_NW, L.kv_blocks, L.kv_tiles, true, false,
                    &p.pattern_kv, s);
   if (e == hipSuccess)
-    e = build_list(in, base + L.bitmap + L.fwd + L.kv, L.q_R, L.q_T, L.q_NW, L.q_blocks, L.q_tiles, false, false,
-                   &p.pattern_q, s);
+    e = build_list(in, base + L.off_q, L.q_R, L.q_T, L.q_NW, L.q_blocks, L.q_tiles, false, false, &p.pattern_q, s);
   if (e == hipSuccess) e = exattn::launch_bwd_bf16(p, exattn::kStageAll, s);
   return from_hip(e);
 }

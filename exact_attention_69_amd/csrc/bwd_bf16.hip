@@ -36,17 +36,47 @@ struct KvCfg {
   static constexpr int WPE = D == 256 ? 1 : 2;  // waves per SIMD
 };
 
-// MODE: kMaskNone, kMaskWindow (contiguous band of query tiles) or
-// kMaskPattern (the workgroup's tile list from the pattern plan).
+// Waves per workgroup: the full-key pass gathers kFullRows keys.
 template <int D, int MODE>
-__global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_kernel(
+constexpr int kv_waves() {
+  return MODE == kMaskFull ? kFullRows / 32 : KvCfg<D>::NW;
+}
+
+// This workgroup's item of a full-position launch: (head, chunk, group of
+// positions), chunk-major within a head.  False for the spare workgroups of
+// the launch, which return at once.
+struct FullItem {
+  int rows, groups, chunks, chunk, group, head;
+};
+__device__ __forceinline__ bool full_item(const FullDev& full, int heads, FullItem* f) {
+  f->rows = full.info[kFullCount];
+  f->groups = full.info[kFullGroups];
+  f->chunks = full.info[kFullChunks];
+  const int per_head = f->groups * f->chunks;
+  const int item = blockIdx.x;
+  if (item >= heads * per_head) return false;
+  f->head = item / per_head;
+  const int r = item - f->head * per_head;
+  f->chunk = r / f->groups;
+  f->group = r - f->chunk * f->groups;
+  return true;
+}
+
+// MODE: kMaskNone, kMaskWindow (contiguous band of query tiles),
+// kMaskPattern (the workgroup's tile list from the pattern plan; full keys
+// are left to the full-key pass) or kMaskFull (a pattern's full keys,
+// gathered, against one chunk of query tiles; with several chunks the
+// partial dK, dV go to the partial buffer).
+template <int D, int MODE>
+__global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd_kv_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int n, int n_kblocks, int total_blocks, float scale,
-    float scale_log2, int window, int group, PatternDev pat) {
+    float scale_log2, int window, int group, PatternDev pat, FullDev full) {
   constexpr bool WINDOWED = MODE == kMaskWindow;
   constexpr bool PATTERN = MODE == kMaskPattern;
-  constexpr int NW = KvCfg<D>::NW;
+  constexpr bool FULL = MODE == kMaskFull;
+  constexpr int NW = kv_waves<D, MODE>();
   constexpr int BQ = KvCfg<D>::BQ;
   constexpr int NT = NW * 64;
   constexpr int BKV = 32 * NW;
@@ -58,9 +88,17 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   __shared__ __attribute__((aligned(16))) __bf16 vres[BKV * D];        // this block's V rows
   __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE*log2(e) / D]
 
-  const int bid = xcd_remap(blockIdx.x, total_blocks);
-  const int kvh = bid / n_kblocks;  // key/value head (batch-major)
-  const int kblk = bid - kvh * n_kblocks;
+  int kvh, kblk;  // key/value head (batch-major), key block
+  FullItem f{};
+  if constexpr (FULL) {
+    if (!full_item(full, total_blocks / n_kblocks, &f)) return;  // whole workgroup: no barrier skipped
+    kvh = f.head;
+    kblk = 0;
+  } else {
+    const int bid = xcd_remap(blockIdx.x, total_blocks);
+    kvh = bid / n_kblocks;
+    kblk = bid - kvh * n_kblocks;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
 
   // The group's query heads kvh*group .. kvh*group + group - 1 all attend to
@@ -69,7 +107,9 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   const int qh0 = kvh * group;
 
   const int kb0 = kblk * BKV;
-  const int my_key = kb0 + wave * 32 + l32;
+  // full keys: slot of the full-key list; slots past the list count as past n
+  const int f_slot = f.group * BKV + wave * 32 + l32;
+  const int my_key = FULL ? (f_slot < f.rows ? full.idx[f_slot] : n) : kb0 + wave * 32 + l32;
 
   // K row of this lane's key as an MFMA B operand (k along d), in registers;
   // the block's V rows (B operand of dP = dO V^T) stay resident in LDS.
@@ -83,10 +123,19 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   }
   // V rows of this block, resident in LDS (visible after the first barrier);
   // key rows past n are clamped copies and only feed unstored dK/dV rows.
-  TileAsync<D, BKV, NT>::issue(Vg + hoff + (size_t)kb0 * D, n - kb0, vres, tid);
+  if constexpr (FULL)
+    TileAsyncRows<D, BKV, NT>::issue(Vg + hoff, full.idx + f.group * BKV, min(BKV, f.rows - f.group * BKV), vres,
+                                     tid);
+  else
+    TileAsync<D, BKV, NT>::issue(Vg + hoff + (size_t)kb0 * D, n - kb0, vres, tid);
 
   int q_lo = 0, q_hi = n;
   if constexpr (WINDOWED) band_keys(kb0, kb0 + BKV, n, window, &q_lo, &q_hi);
+  if constexpr (FULL) {
+    const int tl = full.info[kFullTilesPerChunk];
+    q_lo = f.chunk * tl * BQ;
+    q_hi = min(n, q_lo + tl * BQ);
+  }
   const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
   // query tiles visited: a contiguous range, or the pattern plan's list
   const int* plist = PATTERN ? pat.list + (size_t)kblk * pat.stride : nullptr;
@@ -104,6 +153,12 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
   }
   const unsigned row_span = (unsigned)max(row_hi - row_lo, 0);
   const bool key_global = PATTERN && bit_of(pat.gbits, my_key);
+  // Under a pattern a wave skips the work of a partial query tile where none
+  // of its keys is seen (the layout misses the wave, the band misses its keys
+  // and the tile holds no global row), and of every tile when its keys are
+  // all full keys or past n; loads and barriers stay shared.
+  const int kw0 = kb0 + wave * 32;  // first key of this wave
+  const bool wave_live = !PATTERN || (kw0 < n && pat.own_full[kw0 >> 5] != ~0u);
 
   // Q and dO tiles, and the LSE*log2(e) and D values of their rows, go
   // straight from global memory to LDS.  Rows past n are clamped copies of
@@ -151,68 +206,94 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64, KvCfg<D>::WPE) void bwd_kv_bf16_
     const __bf16* dOs = tiles[buf][1];
     const int i0 = t * BQ;
 
-    // S = Q K^T and dP = dO V^T, lanes indexed by key, registers by query row.
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      s = mfma32(lds_row_frag<D>(Qs, l32, ds, hi), kreg[ds], s);
-      dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), lds_row_frag<D>(vres, wave * 32 + l32, ds, hi), dp);
-    }
-
-    // With a window, queries outside this lane's key band get P = 0 (rows
-    // past n already have P = 0 through their LSE).  Under a pattern, a
-    // partial tile keeps the pairs that the band, a global row, a global key
-    // or the layout make visible.
-    bool need_mask = false;
-    uint32_t gq = 0;  // global bits of the tile's rows, shifted to this lane's half
-    if constexpr (WINDOWED) {
-      const int k_lo_w = kb0 + wave * 32;
-      need_mask = max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
-    }
-    uint32_t any_key = 0;  // this lane's key is global, or the layout covers the wave
+    bool act = true;
     if constexpr (PATTERN) {
       const int entry = plist[it];
-      need_mask = entry & 1;
-      any_key = (uint32_t)key_global | (uint32_t)((entry >> (1 + wave)) & 1);
-      gq = pat.gbits[t] >> (4 * hi);  // BQ = 32: one bitmap word per tile
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int rb = 8 * g + 4 * hi;  // rows rb .. rb+3 of the tile
-      const f32x4 l4 = *(const f32x4*)(&rowst[buf][0][rb]);
-      const f32x4 d4 = *(const f32x4*)(&rowst[buf][1][rb]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * g + j;
-        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j]));
-        // queries that see this lane's key: [row_lo, row_lo + row_span)
-        if (WINDOWED && need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
-        if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
-          const uint32_t vis = (uint32_t)((unsigned)(i0 + rb + j - row_lo) < row_span) | any_key |
-                               ((gq >> (8 * g + j)) & 1u);
-          p = vis ? p : 0.0f;
-        }
-        s[r] = p;
-        dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
+      act = wave_live;
+      if (act && (entry & 1)) {
+        const bool lay = (entry >> (1 + wave)) & 1;
+        const bool band = pat.window >= 0 && i0 <= kw0 + 31 + pat.window && kw0 <= i0 + BQ - 1 + pat.window;
+        act = lay || band || pat.gbits[t] != 0u;  // BQ = 32: one bitmap word per tile
       }
     }
+    if (act) {
+      // S = Q K^T and dP = dO V^T, lanes indexed by key, registers by query row.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        s = mfma32(lds_row_frag<D>(Qs, l32, ds, hi), kreg[ds], s);
+        dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), lds_row_frag<D>(vres, wave * 32 + l32, ds, hi), dp);
+      }
 
-    // dV^T += dO^T P and dK^T += Q^T dS, k along the tile's query rows.
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const bf16x8 pb = acc_to_operand(s, half);
-      const bf16x8 sb = acc_to_operand(dp, half);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv[db] = mfma32(lds_col_frag<D>(dOs, 16 * half, 32 * db, lane), pb, dv[db]);
-        dk[db] = mfma32(lds_col_frag<D>(Qs, 16 * half, 32 * db, lane), sb, dk[db]);
+      // With a window, queries outside this lane's key band get P = 0 (rows
+      // past n already have P = 0 through their LSE).  Under a pattern, a
+      // partial tile keeps the pairs that the band, a global row, a global key
+      // or the layout make visible.
+      bool need_mask = false;
+      uint32_t gq = 0;  // global bits of the tile's rows, shifted to this lane's half
+      if constexpr (WINDOWED) {
+        const int k_lo_w = kb0 + wave * 32;
+        need_mask = max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
       }
+      uint32_t any_key = 0;  // this lane's key is global, or the layout covers the wave
+      if constexpr (PATTERN) {
+        const int entry = plist[it];
+        need_mask = entry & 1;
+        any_key = (uint32_t)key_global | (uint32_t)((entry >> (1 + wave)) & 1);
+        gq = pat.gbits[t] >> (4 * hi);  // BQ = 32: one bitmap word per tile
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rb = 8 * g + 4 * hi;  // rows rb .. rb+3 of the tile
+        const f32x4 l4 = *(const f32x4*)(&rowst[buf][0][rb]);
+        const f32x4 d4 = *(const f32x4*)(&rowst[buf][1][rb]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j]));
+          // queries that see this lane's key: [row_lo, row_lo + row_span)
+          if (WINDOWED && need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
+          if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
+            const uint32_t vis = (uint32_t)((unsigned)(i0 + rb + j - row_lo) < row_span) | any_key |
+                                 ((gq >> (8 * g + j)) & 1u);
+            p = vis ? p : 0.0f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
+        }
+      }
+
+      // dV^T += dO^T P and dK^T += Q^T dS, k along the tile's query rows.
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 pb = acc_to_operand(s, half);
+        const bf16x8 sb = acc_to_operand(dp, half);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv[db] = mfma32(lds_col_frag<D>(dOs, 16 * half, 32 * db, lane), pb, dv[db]);
+          dk[db] = mfma32(lds_col_frag<D>(Qs, 16 * half, 32 * db, lane), sb, dk[db]);
+        }
+      }
+
     }
 
     wait_all_and_barrier();
   }
 
-  if (my_key < n) {
+  bool store = my_key < n;
+  if constexpr (PATTERN) store = store && !bit_of(pat.own_full, my_key);
+  if (FULL && store && f.chunks > 1) {
+    float* prow = full.part + ((size_t)(kvh * f.chunks + f.chunk) * f.groups * BKV + f_slot) * (2 * D);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hi;
+        *(f32x4*)(prow + dd) = f32x4{dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
+                                     dk[db][4 * g + 3] * scale};
+        *(f32x4*)(prow + D + dd) = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+      }
+  } else if (store) {
     __bf16* dkr = dKg + hoff + (size_t)my_key * D;
     __bf16* dvr = dVg + hoff + (size_t)my_key * D;
 #pragma unroll
@@ -250,14 +331,22 @@ struct QCfg<256> {
 };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_kernel(
+constexpr int q_waves() {
+  return MODE == kMaskFull ? kFullRows / 32 : QCfg<D>::NW;
+}
+
+// MODE as for the key side, with query rows owned: kMaskFull gathers a
+// pattern's full rows against one chunk of key tiles.
+template <int D, int MODE>
+__global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
     __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window,
-    int group, PatternDev pat) {
+    int group, PatternDev pat, FullDev full) {
   constexpr bool WINDOWED = MODE == kMaskWindow;
   constexpr bool PATTERN = MODE == kMaskPattern;
-  constexpr int NW = QCfg<D>::NW;
+  constexpr bool FULL = MODE == kMaskFull;
+  constexpr int NW = q_waves<D, MODE>();
   constexpr int BC = QCfg<D>::BC;
   constexpr int NT = NW * 64;
   constexpr int BR = 32 * NW;
@@ -267,9 +356,17 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
 
   __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BC * D];  // [buf][K/V]
 
-  const int bid = xcd_remap(blockIdx.x, total_blocks);
-  const int head = bid / n_qblocks;
-  const int qb = bid - head * n_qblocks;
+  int head, qb;
+  FullItem f{};
+  if constexpr (FULL) {
+    if (!full_item(full, total_blocks / n_qblocks, &f)) return;  // whole workgroup: no barrier skipped
+    head = f.head;
+    qb = 0;
+  } else {
+    const int bid = xcd_remap(blockIdx.x, total_blocks);
+    head = bid / n_qblocks;
+    qb = bid - head * n_qblocks;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
 
   const size_t hoff = (size_t)head * n * D;
@@ -277,7 +374,9 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
   const __bf16* K = Kg + kv_off;
   const __bf16* V = Vg + kv_off;
   const int q0 = qb * BR;
-  const int my_row = q0 + wave * 32 + l32;
+  // full rows: slot of the full-row list; slots past the list count as past n
+  const int f_slot = f.group * BR + wave * 32 + l32;
+  const int my_row = FULL ? (f_slot < f.rows ? full.idx[f_slot] : n) : q0 + wave * 32 + l32;
 
   bf16x8 qreg[NDS], greg[NDS];
   float lse2, dl;
@@ -297,6 +396,11 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
 
   int k_lo = 0, k_hi = n;
   if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
+  if constexpr (FULL) {
+    const int tl = full.info[kFullTilesPerChunk];
+    k_lo = f.chunk * tl * BC;
+    k_hi = min(n, k_lo + tl * BC);
+  }
   const int t_lo = k_lo / BC, t_hi = (k_hi + BC - 1) / BC;
   // key tiles visited: a contiguous range, or the pattern plan's list
   const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
@@ -313,6 +417,10 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
   }
   const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
   const bool row_global = PATTERN && bit_of(pat.gbits, my_row);
+  // Under a pattern a wave skips the work of a partial key tile that none of
+  // its rows sees, and of every tile when its rows are all full rows or past n.
+  const int rw0 = q0 + wave * 32;  // first row of this wave
+  const bool wave_live = !PATTERN || (rw0 < n && pat.own_full[rw0 >> 5] != ~0u);
 
   // K and V tiles go straight from global memory to LDS.  Key rows past n
   // are zeros in the K tile, so whatever their dS, they add exactly nothing
@@ -340,64 +448,92 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
     const __bf16* Vs = tiles[buf][1];
     const int kbase = t * BC;
 
-    // S^T = K Q^T and dP^T = V dO^T: lanes indexed by query row.
-    f32x16 s[NKB], dp[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
-        dp[kb] = mfma32(lds_row_frag<D>(Vs, kb * 32 + l32, ds, hi), greg[ds], dp[kb]);
-      }
-    }
-
-    // With a window, keys outside this lane's row band get P = 0 (keys past
-    // n meet zero K rows).  Under a pattern, a partial tile keeps the pairs
-    // that the band, a global row, a global key or the layout make visible.
-    bool need_mask = false;
-    uint32_t any_row = 0;  // this lane's row is global, or the layout covers the wave
-    if constexpr (WINDOWED) {
-      const int r_lo = q0 + wave * 32;
-      need_mask = max(r_lo + 31 - kbase, kbase + BC - 1 - r_lo) > window;
-    }
+    bool act = true;
     if constexpr (PATTERN) {
       const int entry = plist[it];
-      need_mask = entry & 1;
-      any_row = (uint32_t)row_global | (uint32_t)((entry >> (1 + wave)) & 1);
+      act = wave_live;
+      if (act && (entry & 1)) {
+        const bool lay = (entry >> (1 + wave)) & 1;
+        const bool band = pat.window >= 0 && kbase <= rw0 + 31 + pat.window && rw0 <= kbase + BC - 1 + pat.window;
+        uint32_t g = 0u;
+#pragma unroll
+        for (int w = 0; w < BC / 32; ++w) g |= pat.gbits[(kbase >> 5) + w];
+        act = lay || band || g != 0u;
+      }
     }
+    if (act) {
+      // S^T = K Q^T and dP^T = V dO^T: lanes indexed by query row.
+      f32x16 s[NKB], dp[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
-        if (WINDOWED && need_mask) {
-          const int key = kbase + kb * 32 + acc_row(r, lane);
-          p = (unsigned)(key - key_lo) < key_span ? p : 0.0f;
+        for (int ds = 0; ds < NDS; ++ds) {
+          s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
+          dp[kb] = mfma32(lds_row_frag<D>(Vs, kb * 32 + l32, ds, hi), greg[ds], dp[kb]);
         }
-        if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
-          const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
-          const int key = kbase + kb * 32 + e + 4 * hi;
-          const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);
-          const uint32_t vis = (uint32_t)((unsigned)(key - key_lo) < key_span) | any_row | ((gk >> e) & 1u);
-          p = vis ? p : 0.0f;
-        }
-        dp[kb][r] = p * (dp[kb][r] - dl);  // dS^T (unscaled)
       }
 
-    // dQ^T += K^T dS^T, k along the tile's keys.
+      // With a window, keys outside this lane's row band get P = 0 (keys past
+      // n meet zero K rows).  Under a pattern, a partial tile keeps the pairs
+      // that the band, a global row, a global key or the layout make visible.
+      bool need_mask = false;
+      uint32_t any_row = 0;  // this lane's row is global, or the layout covers the wave
+      if constexpr (WINDOWED) {
+        const int r_lo = q0 + wave * 32;
+        need_mask = max(r_lo + 31 - kbase, kbase + BC - 1 - r_lo) > window;
+      }
+      if constexpr (PATTERN) {
+        const int entry = plist[it];
+        need_mask = entry & 1;
+        any_row = (uint32_t)row_global | (uint32_t)((entry >> (1 + wave)) & 1);
+      }
 #pragma unroll
-    for (int st = 0; st < BC / 16; ++st) {
-      const bf16x8 sb = acc_to_operand(dp[st >> 1], st & 1);
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(lds_col_frag<D>(Ks, 16 * st, 32 * db, lane), sb, dq[db]);
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
+          if (WINDOWED && need_mask) {
+            const int key = kbase + kb * 32 + acc_row(r, lane);
+            p = (unsigned)(key - key_lo) < key_span ? p : 0.0f;
+          }
+          if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
+            const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
+            const int key = kbase + kb * 32 + e + 4 * hi;
+            const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);
+            const uint32_t vis = (uint32_t)((unsigned)(key - key_lo) < key_span) | any_row | ((gk >> e) & 1u);
+            p = vis ? p : 0.0f;
+          }
+          dp[kb][r] = p * (dp[kb][r] - dl);  // dS^T (unscaled)
+        }
+
+      // dQ^T += K^T dS^T, k along the tile's keys.
+#pragma unroll
+      for (int st = 0; st < BC / 16; ++st) {
+        const bf16x8 sb = acc_to_operand(dp[st >> 1], st & 1);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dq[db] = mfma32(lds_col_frag<D>(Ks, 16 * st, 32 * db, lane), sb, dq[db]);
+      }
+
     }
 
     wait_all_and_barrier();
   }
 
-  if (my_row < n) {
+  bool store = my_row < n;
+  if constexpr (PATTERN) store = store && !bit_of(pat.own_full, my_row);
+  if (FULL && store && f.chunks > 1) {
+    float* prow = full.part + ((size_t)(head * f.chunks + f.chunk) * f.groups * BR + f_slot) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hi;
+        *(f32x4*)(prow + dd) = f32x4{dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale, dq[db][4 * g + 2] * scale,
+                                     dq[db][4 * g + 3] * scale};
+      }
+  } else if (store) {
     __bf16* dqr = dQg + hoff + (size_t)my_row * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -412,38 +548,97 @@ __global__ __launch_bounds__(QCfg<D>::NW * 64, QCfg<D>::WPE) void bwd_q_bf16_ker
   }
 }
 
+// Sum of the full positions' chunks (when there are several), in chunk
+// order: each slot holds NOUT vectors of D floats (dK then dV, or dQ), the
+// sums go to out[0..NOUT) at the position's row, in bf16.  One wave per
+// (head, position), in a grid-stride loop.
+template <int D, int NOUT>
+__global__ __launch_bounds__(256) void full_sum_kernel(FullDev full, __bf16* __restrict__ out0,
+                                                       __bf16* __restrict__ out1, int n, int heads) {
+  constexpr int PER = D / 64;  // elements per lane
+  const int R = full.info[kFullCount], C = full.info[kFullChunks];
+  if (C <= 1) return;
+  const size_t GB = (size_t)full.info[kFullGroups] * kFullRows;  // slots per (head, chunk)
+  const int lane = threadIdx.x & 63;
+  const long nwaves = (long)gridDim.x * (blockDim.x >> 6);
+  const long items = (long)heads * R;
+  for (long it = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); it < items; it += nwaves) {
+    const int head = (int)(it / R), slot = (int)(it - (long)head * R);
+    const size_t s0 = (size_t)head * C * GB + slot;
+    const size_t dst = ((size_t)head * n + full.idx[slot]) * D + lane * PER;
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k) {
+      float acc[PER] = {};
+      for (int c = 0; c < C; ++c) {
+        const float* src = full.part + (s0 + c * GB) * (NOUT * D) + k * D + lane * PER;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += src[i];
+      }
+      __bf16* o = k == 0 ? out0 : out1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[dst + i] = (__bf16)acc[i];
+    }
+  }
+}
+
+// Key side, then query side, of one mask mode.
 template <int D, int W>
-hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
+hipError_t bwd_passes(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const float scale_log2 = p.scale * kLog2e;
   const long heads = (long)p.B * p.H;
   const long kv_heads = heads / p.group;
-  constexpr int BKV = 32 * KvCfg<D>::NW;
+  constexpr int BKV = 32 * kv_waves<D, W>();
   const int nkb = (p.n + BKV - 1) / BKV;
   const long tk = (long)nkb * kv_heads;
-  constexpr int BR = 32 * QCfg<D>::NW;
+  constexpr int BR = 32 * q_waves<D, W>();
   const int nqb = (p.n + BR - 1) / BR;
   const long tq = (long)nqb * heads;
   if (tk > 0x7fffffffL || tq > 0x7fffffffL) return hipErrorInvalidValue;
-
-  if (stages & kStageRowdot) {
-    hipError_t e = launch_rowdot<__bf16>((const __bf16*)p.o, (const __bf16*)p.dout, p.lse, p.delta, p.lse2,
-                                         heads * p.n, D, stream);
-    if (e != hipSuccess) return e;
-  }
+  const PatternDev pkv = W == kMaskFull ? PatternDev{} : p.pattern_kv;
+  const PatternDev pq = W == kMaskFull ? PatternDev{} : p.pattern_q;
   if (stages & kStageKV) {
-    hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(KvCfg<D>::NW * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_kv_bf16_kernel<D, W>), dim3((unsigned)tk), dim3(kv_waves<D, W>() * 64), 0, stream,
                        (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
                        p.delta, (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window,
-                       p.group, p.pattern_kv);
+                       p.group, pkv, p.full_kv);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && W == kMaskFull) {
+      hipLaunchKernelGGL((full_sum_kernel<D, 2>), dim3(256), dim3(256), 0, stream, p.full_kv, (__bf16*)p.dk,
+                         (__bf16*)p.dv, p.n, (int)kv_heads);
+      e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
   }
   if (stages & kStageQ) {
-    hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(QCfg<D>::NW * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(q_waves<D, W>() * 64), 0, stream,
                        (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
-                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group,
-                       p.pattern_q);
+                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group, pq,
+                       p.full_q);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && W == kMaskFull) {
+      hipLaunchKernelGGL((full_sum_kernel<D, 1>), dim3(256), dim3(256), 0, stream, p.full_q, (__bf16*)p.dq,
+                         (__bf16*)nullptr, p.n, (int)heads);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Under a pattern with full positions, each side's pattern pass is followed
+// by its full-position pass; the two sides use the partial buffer in turn.
+template <int D, int W>
+hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
+  if (stages & kStageRowdot) {
+    hipError_t e = launch_rowdot<__bf16>((const __bf16*)p.o, (const __bf16*)p.dout, p.lse, p.delta, p.lse2,
+                                         (long)p.B * p.H * p.n, D, stream);
+    if (e != hipSuccess) return e;
+  }
+  const bool with_full = W == kMaskPattern && p.full_kv.idx != nullptr;
+  for (unsigned side : {unsigned(kStageKV), unsigned(kStageQ)}) {
+    if (!(stages & side)) continue;
+    hipError_t e = bwd_passes<D, W>(p, side, stream);
+    if (e == hipSuccess && with_full) e = bwd_passes<D, kMaskFull>(p, side, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

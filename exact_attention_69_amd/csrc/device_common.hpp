@@ -206,6 +206,29 @@ struct TileAsyncZeroTail {
   }
 };
 
+// As TileAsync, but tile row r comes from row rows[r] of `src`; rows at or
+// beyond `valid` are copied from kZeroRow (no index is read for them).
+template <int D, int ROWS, int NT>
+struct TileAsyncRows {
+  static_assert(D <= 256, "kZeroRow holds 256 elements");
+  static constexpr int CPR = D / 8;
+  static constexpr int IT = ROWS * CPR / NT;
+  static_assert((ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
+  static __device__ __forceinline__ void issue(const __bf16* __restrict__ src, const int* __restrict__ rows, int valid,
+                                               __bf16* lds, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int slot0 = it * NT + wave * 64;
+      const int p = slot0 + lane;
+      const int row = p / CPR;
+      const int c = swz_chunk<D>(row, p % CPR);
+      lds_dma16(row < valid ? (const void*)(src + (size_t)rows[row] * D + 8 * c) : (const void*)(kZeroRow + 8 * c),
+                lds + 8 * slot0);
+    }
+  }
+};
+
 // Wait for every outstanding memory operation of this wave (including direct
 // global -> LDS copies), then synchronise the workgroup.
 __device__ __forceinline__ void wait_all_and_barrier() {

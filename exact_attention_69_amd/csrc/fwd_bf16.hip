@@ -57,17 +57,27 @@ struct FwdCfg<256> {
   static constexpr int NW = 4, RB = 1, BC = 32, WPE = 1;
 };
 
-// MODE: kMaskNone, kMaskWindow (contiguous band of key tiles, analytic
-// masks), or kMaskPattern (the workgroup's tile list from the pattern plan;
-// the union mask on partial tiles).
+// Waves per workgroup: the full-row pass gathers kFullRows rows.
 template <int D, int MODE>
-__global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_kernel(
+constexpr int fwd_waves() {
+  return MODE == kMaskFull ? kFullRows / 32 : FwdCfg<D>::NW;
+}
+
+// MODE: kMaskNone, kMaskWindow (contiguous band of key tiles, analytic
+// masks), kMaskPattern (the workgroup's tile list from the pattern plan; the
+// union mask on partial tiles; full rows are left to the full-row pass), or
+// kMaskFull (a pattern's full rows, gathered, against one chunk of key tiles;
+// with several chunks the normalised partial O and its log-sum-exp go to the
+// partial buffers).
+template <int D, int MODE>
+__global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void fwd_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n_qblocks, int total_blocks,
-    float scale_log2, int window, int group, PatternDev pat) {
+    float scale_log2, int window, int group, PatternDev pat, FullDev full) {
   constexpr bool WINDOWED = MODE == kMaskWindow;
   constexpr bool PATTERN = MODE == kMaskPattern;
-  constexpr int NW = FwdCfg<D>::NW;
+  constexpr bool FULL = MODE == kMaskFull;
+  constexpr int NW = fwd_waves<D, MODE>();
   constexpr int RB = FwdCfg<D>::RB;
   constexpr int BC = FwdCfg<D>::BC;
   constexpr int BR = 32 * RB * NW;
@@ -79,9 +89,26 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 vbuf[2][BC * D];
 
-  const int bid = xcd_remap(blockIdx.x, total_blocks);
-  const int head = bid / n_qblocks;
-  const int qb = bid - head * n_qblocks;
+  int head, qb;
+  // full rows: this workgroup's chunk and group of rows
+  int f_rows = 0, f_groups = 0, f_chunks = 1, f_chunk = 0, f_group = 0;
+  if constexpr (FULL) {
+    f_rows = full.info[kFullCount];
+    f_groups = full.info[kFullGroups];
+    f_chunks = full.info[kFullChunks];
+    const int per_head = f_groups * f_chunks;
+    const int item = blockIdx.x;
+    if (item >= (total_blocks / n_qblocks) * per_head) return;  // whole workgroup: no barrier skipped
+    head = item / per_head;
+    const int r = item - head * per_head;
+    f_chunk = r / f_groups;
+    f_group = r - f_chunk * f_groups;
+    qb = 0;
+  } else {
+    const int bid = xcd_remap(blockIdx.x, total_blocks);
+    head = bid / n_qblocks;
+    qb = bid - head * n_qblocks;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,7 +128,14 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   const int w0 = q0 + wave * 32 * RB;  // first row of this wave
   int my_row[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) my_row[rb] = w0 + 32 * rb + l32;
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (FULL) {  // slot of the full-row list; rows past the list count as past n
+      const int slot = f_group * BR + wave * 32 * RB + 32 * rb + l32;
+      my_row[rb] = slot < f_rows ? full.idx[slot] : n;
+    } else {
+      my_row[rb] = w0 + 32 * rb + l32;
+    }
+  }
 
   // Q^T operands, kept in registers: lane holds Q[my_row][16*ds + 8*hi .. +8].
   bf16x8 qreg[RB][NDS];
@@ -118,6 +152,11 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   // block for a window), or the block's list from the pattern plan.
   int k_lo = 0, k_hi = n;
   if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
+  if constexpr (FULL) {
+    const int tl = full.info[kFullTilesPerChunk];
+    k_lo = f_chunk * tl * BC;
+    k_hi = min(n, k_lo + tl * BC);
+  }
   const int t_lo = k_lo / BC;
   const int t_hi = (k_hi + BC - 1) / BC;
   const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
@@ -186,8 +225,33 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     if (n_tiles > 1) issue_k(tile_at(1), kbuf[1]);
   }
   wait_all_and_barrier();
+
+  // Under a pattern a wave skips the work of a partial tile where none of its
+  // rows sees a key (the layout misses the wave, the band misses its rows and
+  // the tile holds no global key), and of every tile when its rows are all
+  // full rows or past n; the loads and barriers stay shared by the workgroup.
+  bool wave_live = true;
+  if constexpr (PATTERN) wave_live = w0 < n && pat.own_full[w0 >> 5] != ~0u;
+  auto wave_sees = [&](int i) -> bool {
+    if constexpr (!PATTERN) {
+      return true;
+    } else {
+      const int entry = plist[i];
+      if (!wave_live) return false;
+      if (!(entry & 1)) return true;
+      const int c0 = (entry >> kEntryTileShift) * BC;
+      bool a = (entry >> (1 + wave)) & 1;
+      if (pat.window >= 0) a = a || (c0 <= w0 + 31 + pat.window && w0 <= c0 + BC - 1 + pat.window);
+      uint32_t g = 0u;
+#pragma unroll
+      for (int w = 0; w < BC / 32; ++w) g |= pat.gbits[(c0 >> 5) + w];
+      return a || g != 0u;
+    }
+  };
+
   f32x16 s_cur[RB][NKB];
-  compute_s(kbuf[0], s_cur);
+  bool act_cur = !PATTERN || (n_tiles > 0 && wave_sees(0));
+  if (act_cur) compute_s(kbuf[0], s_cur);
 
   for (int j = 0; j < n_tiles; ++j) {
     const int t = tile_at(j);
@@ -197,133 +261,156 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
     if (j + 2 < n_tiles) issue_k(tile_at(j + 2), kbuf[j & 1]);
     const int kbase = t * BC;
 
-    // ---- masks: key tail, sliding window, pattern ---------------------------
-    bool need_mask = kbase + BC > n;
-    if constexpr (WINDOWED) {
-      const int r_hi = w0 + 32 * RB - 1;
-      need_mask = need_mask || max(r_hi - kbase, kbase + BC - 1 - w0) > window;
-    }
-    if constexpr (PATTERN) {
-      const int entry = plist[j];
-      if (entry & 1) {
-        static_assert(RB == 1 && BC % 32 == 0, "pattern masks assume one 32-row block per wave");
-        // visible: key < n and (band or global row or global key or the
-        // layout covers this wave's rows for the tile).  Evaluated with
-        // bitwise operators into one select per element: no short-circuit
-        // branches.
-        const uint32_t any_row = (uint32_t)row_global[0] | (uint32_t)((entry >> (1 + wave)) & 1);
+    const bool act_next = !PATTERN || (j + 1 < n_tiles && wave_sees(j + 1));
+    if (act_cur) {
+      // ---- masks: key tail, sliding window, pattern ---------------------------
+      bool need_mask = kbase + BC > n;
+      if constexpr (WINDOWED) {
+        const int r_hi = w0 + 32 * RB - 1;
+        need_mask = need_mask || max(r_hi - kbase, kbase + BC - 1 - w0) > window;
+      }
+      if constexpr (PATTERN) {
+        const int entry = plist[j];
+        if (entry & 1) {
+          static_assert(RB == 1 && BC % 32 == 0, "pattern masks assume one 32-row block per wave");
+          // visible: key < n and (band or global row or global key or the
+          // layout covers this wave's rows for the tile).  Evaluated with
+          // bitwise operators into one select per element: no short-circuit
+          // branches.
+          const uint32_t any_row = (uint32_t)row_global[0] | (uint32_t)((entry >> (1 + wave)) & 1);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);  // keys kbase+32kb+4hi+..
+          for (int kb = 0; kb < NKB; ++kb) {
+            const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);  // keys kbase+32kb+4hi+..
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
-            const int key = kbase + kb * 32 + e + 4 * hi;
-            const uint32_t vis = (uint32_t)(key < n) &
-                                 ((uint32_t)((unsigned)(key - key_lo[0]) < key_span[0]) | any_row | ((gk >> e) & 1u));
-            s_cur[0][kb][r] = vis ? s_cur[0][kb][r] : kNegInf;
+            for (int r = 0; r < 16; ++r) {
+              const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
+              const int key = kbase + kb * 32 + e + 4 * hi;
+              const uint32_t vis = (uint32_t)(key < n) &
+                                   ((uint32_t)((unsigned)(key - key_lo[0]) < key_span[0]) | any_row | ((gk >> e) & 1u));
+              s_cur[0][kb][r] = vis ? s_cur[0][kb][r] : kNegInf;
+            }
           }
         }
-      }
-    } else if (need_mask) {
+      } else if (need_mask) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbase + kb * 32 + acc_row(r, lane);
+              s_cur[rb][kb][r] = (unsigned)(key - key_lo[rb]) < key_span[rb] ? s_cur[rb][kb][r] : kNegInf;
+            }
+      }
+
+      // ---- running max and (rare) rescale -------------------------------------
+      float msub[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + kb * 32 + acc_row(r, lane);
-            s_cur[rb][kb][r] = (unsigned)(key - key_lo[rb]) < key_span[rb] ? s_cur[rb][kb][r] : kNegInf;
-          }
-    }
-
-    // ---- running max and (rare) rescale -------------------------------------
-    float msub[RB];
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[rb][kb][r]);
+        mx = pair_max(mx);
+        const float mx2 = mx * scale_log2;  // -inf stays -inf
+        const bool grow = mx2 > m_run[rb] + kRescaleThreshold || (m_run[rb] == kNegInf && mx2 != kNegInf);
+        if (__any(grow)) {
+          const float m_new = grow ? mx2 : m_run[rb];
+          const float alpha = grow ? fast_exp2(m_run[rb] - m_new) : 1.0f;  // m_run=-inf -> 0
+          l_part[rb] *= alpha;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = kNegInf;
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[rb][kb][r]);
-      mx = pair_max(mx);
-      const float mx2 = mx * scale_log2;  // -inf stays -inf
-      const bool grow = mx2 > m_run[rb] + kRescaleThreshold || (m_run[rb] == kNegInf && mx2 != kNegInf);
-      if (__any(grow)) {
-        const float m_new = grow ? mx2 : m_run[rb];
-        const float alpha = grow ? fast_exp2(m_run[rb] - m_new) : 1.0f;  // m_run=-inf -> 0
-        l_part[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
-        m_run[rb] = m_new;
-      }
-      msub[rb] = m_run[rb] == kNegInf ? 0.0f : m_run[rb];
-    }
-
-    // ---- exponentials (vector ALU) || S of the next tile (matrix cores) -----
-    // P of key block kb goes to bf16 (the operand of the P V product); once a
-    // block is converted its fp32 registers receive that block of the next
-    // tile's S, so the next S needs no registers of its own and the
-    // exponentials of block kb+1 run beside the matrix products of block kb.
-    // On the last tile the next S reads a stale K buffer; it is unused.  The
-    // fp32 row sum is split over independent partial sums.
-    bf16x8 pb[RB][BC / 16];
-    float lsum[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lsum[rb][i] = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s_cur[rb][kb][r] = fast_exp2(__builtin_fmaf(s_cur[rb][kb][r], scale_log2, -msub[rb]));
-          lsum[rb][r & 3] += s_cur[rb][kb][r];
+            for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
+          m_run[rb] = m_new;
         }
-        pb[rb][2 * kb] = acc_to_operand(s_cur[rb][kb], 0);
-        pb[rb][2 * kb + 1] = acc_to_operand(s_cur[rb][kb], 1);
+        msub[rb] = m_run[rb] == kNegInf ? 0.0f : m_run[rb];
       }
-      compute_s_block(kbuf[(j + 1) & 1], kb, s_cur);
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l_part[rb] += (lsum[rb][0] + lsum[rb][1]) + (lsum[rb][2] + lsum[rb][3]);
 
-    // ---- O^T += V^T P^T -------------------------------------------------------
-    // A operand (V^T): lane l needs V[key(t)][db*32 + l%32] with the keys in
-    // the k order of pb (the transpose read delivers exactly that).
-    const __bf16* Vs = vbuf[j & 1];
+      // ---- exponentials (vector ALU) || S of the next tile (matrix cores) -----
+      // P of key block kb goes to bf16 (the operand of the P V product); once a
+      // block is converted its fp32 registers receive that block of the next
+      // tile's S, so the next S needs no registers of its own and the
+      // exponentials of block kb+1 run beside the matrix products of block kb.
+      // On the last tile the next S reads a stale K buffer; it is unused.  The
+      // fp32 row sum is split over independent partial sums.
+      bf16x8 pb[RB][BC / 16];
+      float lsum[RB][4];
 #pragma unroll
-    for (int st = 0; st < BC / 16; ++st)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 a = lds_col_frag<D>(Vs, 16 * st, 32 * db, lane);
+        for (int i = 0; i < 4; ++i) lsum[rb][i] = 0.0f;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(a, pb[rb][st], o[rb][db]);
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s_cur[rb][kb][r] = fast_exp2(__builtin_fmaf(s_cur[rb][kb][r], scale_log2, -msub[rb]));
+            lsum[rb][r & 3] += s_cur[rb][kb][r];
+          }
+          pb[rb][2 * kb] = acc_to_operand(s_cur[rb][kb], 0);
+          pb[rb][2 * kb + 1] = acc_to_operand(s_cur[rb][kb], 1);
+        }
+        if (act_next) compute_s_block(kbuf[(j + 1) & 1], kb, s_cur);
       }
-    {
-      constexpr int NP = (BC / 16) * NDB, kLead = 3;
-      EXATTN_SCHED(kSchedDSRead, 2 * kLead);
 #pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        EXATTN_SCHED(kSchedMFMA, RB);
-        if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
+      for (int rb = 0; rb < RB; ++rb) l_part[rb] += (lsum[rb][0] + lsum[rb][1]) + (lsum[rb][2] + lsum[rb][3]);
+
+      // ---- O^T += V^T P^T -------------------------------------------------------
+      // A operand (V^T): lane l needs V[key(t)][db*32 + l%32] with the keys in
+      // the k order of pb (the transpose read delivers exactly that).
+      const __bf16* Vs = vbuf[j & 1];
+#pragma unroll
+      for (int st = 0; st < BC / 16; ++st)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 a = lds_col_frag<D>(Vs, 16 * st, 32 * db, lane);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(a, pb[rb][st], o[rb][db]);
+        }
+      {
+        constexpr int NP = (BC / 16) * NDB, kLead = 3;
+        EXATTN_SCHED(kSchedDSRead, 2 * kLead);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          EXATTN_SCHED(kSchedMFMA, RB);
+          if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
+        }
       }
+    } else if (act_next) {
+      compute_s(kbuf[(j + 1) & 1], s_cur);
     }
+    act_cur = act_next;
 
     wait_all_and_barrier();
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -----------------------
   // A row that saw no key (possible only under a pattern without a window)
-  // gets O = 0 and LSE = -inf.
+  // gets O = 0 and LSE = -inf.  Under a pattern the full rows are left to the
+  // full-row pass; that pass writes partial results when it has several chunks.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = pair_sum(l_part[rb]);
-    if (my_row[rb] < n) {
+    bool store = my_row[rb] < n;
+    if constexpr (PATTERN) store = store && !bit_of(pat.own_full, my_row[rb]);
+    if (FULL && store && f_chunks > 1) {
+      const float inv = 1.0f / l_tot;  // every chunk holds at least one key
+      const size_t slot = (size_t)(head * f_chunks + f_chunk) * f_groups * BR + f_group * BR + wave * 32 * RB +
+                          32 * rb + l32;
+      float* prow = full.part + slot * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dd = db * 32 + 8 * g + 4 * hi;
+          *(f32x4*)(prow + dd) = f32x4{o[rb][db][4 * g] * inv, o[rb][db][4 * g + 1] * inv,
+                                       o[rb][db][4 * g + 2] * inv, o[rb][db][4 * g + 3] * inv};
+        }
+      if (hi == 0) full.part_lse[slot] = kLn2 * (m_run[rb] + fast_log2(l_tot));
+    } else if (store) {
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       __bf16* Orow = Og + head_off + (size_t)my_row[rb] * D;
 #pragma unroll
@@ -341,16 +428,60 @@ __global__ __launch_bounds__(FwdCfg<D>::NW * 64, FwdCfg<D>::WPE) void fwd_bf16_k
   }
 }
 
+// Merge of the full rows' chunks (when there are several): with each
+// chunk's normalised O_c and log-sum-exp L_c, L = log sum_c exp(L_c) and
+// O = sum_c exp(L_c - L) O_c (the two-block merge of the online softmax,
+// applied over all chunks at once).  One wave per (head, full row), in a
+// grid-stride loop; the chunks are read in order, so the result is
+// deterministic.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_full_merge_kernel(FullDev full, __bf16* __restrict__ Og,
+                                                             float* __restrict__ LSEg, int n, int heads) {
+  constexpr int PER = D / 64;  // elements per lane
+  const int R = full.info[kFullCount], C = full.info[kFullChunks];
+  if (C <= 1) return;
+  const size_t GB = (size_t)full.info[kFullGroups] * kFullRows;  // slots per (head, chunk)
+  const int lane = threadIdx.x & 63;
+  const long nwaves = (long)gridDim.x * (blockDim.x >> 6);
+  const long items = (long)heads * R;
+  for (long it = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); it < items; it += nwaves) {
+    const int head = (int)(it / R), slot = (int)(it - (long)head * R);
+    const size_t s0 = (size_t)head * C * GB + slot;
+    float m = kNegInf;
+    for (int c = 0; c < C; ++c) m = fmaxf(m, full.part_lse[s0 + c * GB]);
+    float acc[PER] = {}, l = 0.0f;
+    if (m != kNegInf) {
+      for (int c = 0; c < C; ++c) {
+        const float w = expf(full.part_lse[s0 + c * GB] - m);
+        const float* src = full.part + (s0 + c * GB) * D + lane * PER;
+        l += w;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += w * src[i];
+      }
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int row = full.idx[slot];
+    __bf16* dst = Og + ((size_t)head * n + row) * D + lane * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) dst[i] = (__bf16)(acc[i] * inv);
+    if (lane == 0) LSEg[(size_t)head * n + row] = l > 0.0f ? m + logf(l) : kNegInf;
+  }
+}
+
 template <int D, int MODE>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  constexpr int BR = 32 * FwdCfg<D>::RB * FwdCfg<D>::NW;
+  constexpr int BR = 32 * FwdCfg<D>::RB * fwd_waves<D, MODE>();
   const int nqb = (p.n + BR - 1) / BR;
   const long total = (long)nqb * p.B * p.H;
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
   const float scale_log2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE>), dim3((unsigned)total), dim3(FwdCfg<D>::NW * 64), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE>), dim3((unsigned)total), dim3(fwd_waves<D, MODE>() * 64), 0, stream,
                      (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (__bf16*)p.o, p.lse, p.n,
-                     nqb, (int)total, scale_log2, p.window, p.group, p.pattern);
+                     nqb, (int)total, scale_log2, p.window, p.group, p.pattern, p.full);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || MODE != kMaskFull) return e;
+  hipLaunchKernelGGL((fwd_full_merge_kernel<D>), dim3(256), dim3(256), 0, stream, p.full, (__bf16*)p.o, p.lse, p.n,
+                     p.B * p.H);
   return hipGetLastError();
 }
 
@@ -367,7 +498,11 @@ hipError_t launch_mode(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.pattern.list != nullptr) return launch_mode<kMaskPattern>(p, stream);
+  if (p.pattern.list != nullptr) {
+    const hipError_t e = launch_mode<kMaskPattern>(p, stream);
+    if (e != hipSuccess || p.full.idx == nullptr) return e;
+    return launch_mode<kMaskFull>(p, stream);
+  }
   return p.window >= 0 ? launch_mode<kMaskWindow>(p, stream) : launch_mode<kMaskNone>(p, stream);
 }
 

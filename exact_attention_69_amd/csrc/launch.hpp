@@ -9,7 +9,9 @@
 namespace exattn {
 
 // Masking modes of the kernels.
-enum MaskMode : int { kMaskNone = 0, kMaskWindow = 1, kMaskPattern = 2 };
+// kMaskFull: the full positions of a pattern (rows or keys gathered from the
+// plan's list), each workgroup over one chunk of the other side's tiles.
+enum MaskMode : int { kMaskNone = 0, kMaskWindow = 1, kMaskPattern = 2, kMaskFull = 3 };
 
 struct FwdParams {
   const void* q;
@@ -22,6 +24,7 @@ struct FwdParams {
   int window;  // -1: no mask
   int group;   // query heads per key/value head: K, V are [B, H / group, n, d]
   PatternDev pattern;  // list == nullptr: no pattern
+  FullDev full;        // with a pattern: its full rows (idx == nullptr: none)
 };
 
 struct BwdParams {
@@ -42,6 +45,8 @@ struct BwdParams {
   int group;  // query heads per key/value head: K, V, dK, dV are [B, H / group, n, d]
   PatternDev pattern_kv;  // lists for the key-side pass (list == nullptr: no pattern)
   PatternDev pattern_q;   // lists for the query-side pass
+  FullDev full_kv;        // with a pattern: its full keys
+  FullDev full_q;         // with a pattern: its full rows
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);

@@ -6,7 +6,8 @@
 //   or layout[i / 64][j / 64] is set.
 //
 // A plan step turns the pattern into, for every workgroup of a kernel, the
-// list of tiles it must visit.  Each entry is
+// list of tiles it must visit for the positions it stores (full positions,
+// below, are left to a pass of their own).  Each entry is
 //   bits 9..31  tile index
 //   bits 1..8   per wave: the layout covers this wave's 32 rows (or keys)
 //               for the whole tile
@@ -31,12 +32,47 @@ __host__ __device__ inline int bitmap_words(int n) { return (n + 31) / 32 + kBit
 
 // What a kernel needs at run time.
 struct PatternDev {
-  int window;              // -1: no band term
-  const uint32_t* gbits;   // global-token bitmap (bitmap_words(n) words)
-  const int* list;         // entries, `stride` per workgroup row of the grid
-  const int* count;        // number of entries per workgroup row
+  int window;                // -1: no band term
+  const uint32_t* gbits;     // global-token bitmap (bitmap_words(n) words)
+  const uint32_t* own_full;  // full positions of the side a workgroup owns
+                             // (rows, or keys for the key-side pass): not
+                             // stored, the full-position pass writes them
+  const int* list;           // entries, `stride` per workgroup row of the grid
+  const int* count;          // number of entries per workgroup row
   int stride;
 };
+
+// Full positions: a query row that sees every key (a global token, or a row
+// whose layout row is set in every block), or a key that every query sees
+// (a global token, or a key whose layout column is set in every block).  A
+// workgroup holding one would have to visit every tile of the other side, so
+// they get a pass of their own: workgroups of kFullRows gathered positions,
+// each over one chunk of the other side's tiles, with the chunks' partial
+// results merged afterwards (rows: the two-block log-sum-exp merge; keys and
+// dQ: a sum in chunk order).
+constexpr int kFullRows = 128;
+constexpr int kFullChunkTiles = 16;  // target tiles per chunk
+
+// Per consumer kernel, written by the plan: [0] number of full positions R,
+// [1] workgroups of positions G = ceil(R / kFullRows), [2] chunks C,
+// [3] tiles per chunk.
+enum FullInfo : int { kFullCount = 0, kFullGroups = 1, kFullChunks = 2, kFullTilesPerChunk = 3, kFullInfoInts = 4 };
+
+struct FullDev {
+  const int* idx;   // full positions, ascending
+  const int* info;  // FullInfo
+  float* part;      // partial results (used when C > 1)
+  float* part_lse;  // forward only: partial log-sum-exp
+};
+
+// Partial-result slots per head: at most a quarter of n (rounded up to whole
+// workgroups); with more full positions than that, C = 1 and no partials.
+__host__ __device__ inline int full_part_rows(int n) {
+  const int q = (n + 3) / 4;
+  return (q + kFullRows - 1) / kFullRows * kFullRows;
+}
+// Workgroups per head a full-position launch provides (>= G * C).
+__host__ __device__ inline int full_items_per_head(int n) { return (n + kFullRows - 1) / kFullRows; }
 
 // One list to build: workgroups own `R` consecutive positions (queries, or
 // keys when `transposed`), tiles span `T` positions of the other side, `NW`
@@ -46,6 +82,7 @@ struct PlanList {
   int R, T, NW;
   bool transposed;
   bool tail_partial;
+  const uint32_t* own_full;  // full positions of the owned side: they drive no tile
   int* list;
   int* count;
   int stride;
@@ -60,9 +97,22 @@ struct PlanInput {
   const unsigned char* layout;  // nullptr: no layout
   int layout_n;                 // blocks per layout row
   uint32_t* gbits;              // bitmap to build
+  uint32_t* row_full;           // full query rows (bitmap)
+  uint32_t* col_full;           // full keys (bitmap)
+  int* layout_flags;            // [layout_n] rows set in every block, [layout_n] columns
+  int* row_idx;                 // full rows, ascending (n ints)
+  int* col_idx;                 // full keys, ascending (n ints)
 };
 
-hipError_t launch_pattern_bitmap(const PlanInput& in, hipStream_t stream);
+// How one consumer kernel splits its full positions: `tiles` tiles of the
+// other side; the chosen G, C and tiles per chunk go to `info`.
+struct FullSplit {
+  int tiles;
+  bool keys;  // over the full keys (else the full rows)
+  int* info;
+};
+
+hipError_t launch_pattern_bitmap(const PlanInput& in, const FullSplit* splits, int n_splits, hipStream_t stream);
 hipError_t launch_pattern_list(const PlanInput& in, const PlanList& pl, hipStream_t stream);
 
 // Element visibility on a partial tile, given the per-row and per-key terms.

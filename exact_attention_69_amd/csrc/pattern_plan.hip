@@ -1,20 +1,125 @@
-// Plan kernels for sparse patterns: the global-token bitmap, then for every
-// workgroup of a kernel the list of tiles that hold at least one visible
-// (query, key) pair, each classified as fully visible or partial.
+// Plan kernels for sparse patterns: the global-token bitmap and the full
+// positions, then for every workgroup of a kernel the list of tiles that hold
+// at least one visible (query, key) pair of a position it stores, each
+// classified as fully visible or partial.
 #include "pattern.hpp"
 
 namespace exattn {
 namespace {
 
-// One workgroup: clear the bitmap (padding included), then set the bit of
-// every global position in [0, n); positions outside are ignored.
-__global__ __launch_bounds__(1024) void pattern_bitmap_kernel(const int* __restrict__ gidx, int ng, int n,
-                                                             uint32_t* __restrict__ bits, int nwords) {
-  for (int w = threadIdx.x; w < nwords; w += blockDim.x) bits[w] = 0u;
+// One workgroup per layout block index r: is layout row r set in every
+// block, and is layout column r set in every block?
+__global__ __launch_bounds__(256) void pattern_layout_full_kernel(const unsigned char* __restrict__ layout, int nb,
+                                                                  int* __restrict__ flags) {
+  const int r = blockIdx.x;
+  int row_all = 1, col_all = 1;
+  for (int c = threadIdx.x; c < nb; c += blockDim.x) {
+    row_all &= layout[(size_t)r * nb + c] != 0;
+    col_all &= layout[(size_t)c * nb + r] != 0;
+  }
+  row_all = __syncthreads_and(row_all);
+  col_all = __syncthreads_and(col_all);
+  if (threadIdx.x == 0) {
+    flags[r] = row_all;
+    flags[nb + r] = col_all;
+  }
+}
+
+// Exclusive prefix sum over the workgroup (blockDim.x a multiple of 64, at
+// most 1024); `sh` holds 16 ints.  Returns this thread's offset and the total.
+__device__ int block_exclusive_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  int x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
   __syncthreads();
-  for (int i = threadIdx.x; i < ng; i += blockDim.x) {
-    const int p = gidx[i];
-    if ((unsigned)p < (unsigned)n) atomicOr(&bits[p >> 5], 1u << (p & 31));
+  int before = 0, tot = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const int t = sh[w];
+    before += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();  // sh is reused by the next scan
+  *total = tot;
+  return before + x - v;
+}
+
+// Writes the positions of the set bits of words [w0, w1) from `out[pos]` on.
+__device__ void write_positions(const uint32_t* bits, int w0, int w1, int* out, int pos) {
+  for (int w = w0; w < w1; ++w)
+    for (uint32_t m = bits[w]; m != 0u; m &= m - 1u) out[pos++] = 32 * w + __builtin_ctz(m);
+}
+
+struct FullSplits {
+  FullSplit s[3];
+  int count;
+};
+
+// One workgroup: the global-token bitmap (padding cleared; positions outside
+// [0, n) ignored), the full-row and full-key bitmaps (global tokens, plus the
+// layout rows / columns set in every block), their ascending position lists,
+// and how each consumer kernel splits them into workgroups and chunks.
+__global__ __launch_bounds__(1024) void pattern_bitmap_kernel(PlanInput in, FullSplits sp) {
+  __shared__ int sh[16];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int n = in.n, nwords = bitmap_words(n), W = (n + 31) / 32;
+  for (int w = tid; w < nwords; w += nt) in.gbits[w] = 0u;
+  __syncthreads();
+  for (int i = tid; i < in.n_global; i += nt) {
+    const int p = in.global_idx[i];
+    if ((unsigned)p < (unsigned)n) atomicOr(&in.gbits[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  for (int w = tid; w < nwords; w += nt) {
+    uint32_t r = in.gbits[w], c = r;
+    if (in.layout != nullptr && w < W) {
+      const int b = w / (kLayoutBlock / 32);  // the 32 positions of a word lie in one layout block
+      if (in.layout_flags[b]) r = ~0u;
+      if (in.layout_flags[in.layout_n + b]) c = ~0u;
+      if (32 * w + 32 > n) {
+        const uint32_t keep = (1u << (n - 32 * w)) - 1u;
+        r &= keep;
+        c &= keep;
+      }
+    }
+    in.row_full[w] = r;
+    in.col_full[w] = c;
+  }
+  __syncthreads();
+  // compaction: each thread takes a contiguous run of words
+  const int per = (W + nt - 1) / nt;
+  const int w0 = min(W, tid * per), w1 = min(W, w0 + per);
+  int nr = 0, nc = 0;
+  for (int w = w0; w < w1; ++w) {
+    nr += __builtin_popcount(in.row_full[w]);
+    nc += __builtin_popcount(in.col_full[w]);
+  }
+  int rows_total, cols_total;
+  const int pr = block_exclusive_scan(nr, sh, &rows_total);
+  const int pc = block_exclusive_scan(nc, sh, &cols_total);
+  write_positions(in.row_full, w0, w1, in.row_idx, pr);
+  write_positions(in.col_full, w0, w1, in.col_idx, pc);
+  if (tid == 0) {
+    for (int i = 0; i < sp.count; ++i) {
+      const FullSplit& f = sp.s[i];
+      const int R = f.keys ? cols_total : rows_total;
+      const int G = (R + kFullRows - 1) / kFullRows;
+      int C = 1;
+      if (G > 0) {
+        const int cap = full_part_rows(n) / (kFullRows * G);
+        const int want = (f.tiles + kFullChunkTiles - 1) / kFullChunkTiles;
+        C = max(1, min(cap, want));
+      }
+      const int tl = (f.tiles + C - 1) / C;
+      C = (f.tiles + tl - 1) / tl;  // no empty chunk
+      f.info[kFullCount] = R;
+      f.info[kFullGroups] = G;
+      f.info[kFullChunks] = C;
+      f.info[kFullTilesPerChunk] = tl;
+    }
   }
 }
 
@@ -42,7 +147,10 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
   const int r0 = blk * pl.R, r1 = min(n, r0 + pl.R);  // own positions
   const int n_own = r1 - r0;
   const int g_own = count_bits(in.gbits, r0, r1);
-  const int ntile = (n + pl.T - 1) / pl.T;
+  // Full own positions are written by the full-position pass: they list no
+  // tile, and a block holding only such positions lists none.
+  const bool any_part = n_own > count_bits(pl.own_full, r0, r1);
+  const int ntile = any_part ? (n + pl.T - 1) / pl.T : 0;
   int* out = pl.list + (size_t)blk * pl.stride;
   int total = 0;  // entries written so far (uniform)
   for (int base = 0; base < ntile; base += 256) {
@@ -76,11 +184,13 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
           const bool on =
               in.layout[pl.transposed ? (size_t)tb * in.layout_n + ob : (size_t)ob * in.layout_n + tb] != 0;
           if (on) wbits |= 1u << w;
-          lay_any = lay_any || on;
+          lay_any = lay_any || (on && pl.own_full[p >> 5] != ~0u);  // a wave of full positions needs no tile
           lay_all = lay_all && on;
         }
       }
-      if (any_band || gq > 0 || gk > 0 || lay_any) {
+      // global positions on the owned side are full positions: only the
+      // other side's global term lists a tile
+      if (any_band || g_other > 0 || lay_any) {
         const bool full = full_band || gq == nq || gk == nk || lay_all;
         const bool partial = !full || (pl.tail_partial && c1 - c0 < pl.T);
         entry = (t << kEntryTileShift) | (int)(wbits << 1) | (partial ? 1 : 0);
@@ -102,9 +212,18 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
 
 }  // namespace
 
-hipError_t launch_pattern_bitmap(const PlanInput& in, hipStream_t stream) {
-  hipLaunchKernelGGL(pattern_bitmap_kernel, dim3(1), dim3(1024), 0, stream, in.global_idx, in.n_global, in.n,
-                     in.gbits, bitmap_words(in.n));
+hipError_t launch_pattern_bitmap(const PlanInput& in, const FullSplit* splits, int n_splits, hipStream_t stream) {
+  if (n_splits < 0 || n_splits > 3) return hipErrorInvalidValue;
+  if (in.layout != nullptr) {
+    hipLaunchKernelGGL(pattern_layout_full_kernel, dim3(in.layout_n), dim3(256), 0, stream, in.layout, in.layout_n,
+                       in.layout_flags);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  FullSplits sp{};
+  for (int i = 0; i < n_splits; ++i) sp.s[i] = splits[i];
+  sp.count = n_splits;
+  hipLaunchKernelGGL(pattern_bitmap_kernel, dim3(1), dim3(1024), 0, stream, in, sp);
   return hipGetLastError();
 }
 

@@ -32,15 +32,26 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 KERNEL_RE = re.compile(r"(fwd_bf16_kernel|bwd_kv_bf16_kernel|bwd_q_bf16_kernel|bwd_rowdot_kernel|fwd_f32_kernel|"
-                       r"bwd_kv_f32_kernel|bwd_q_f32_kernel|pattern_bitmap_kernel|pattern_list_kernel|elementwise_kernel|"
-                       r"copy\w*)(?:I\w*?Li(\d+))?")
+                       r"bwd_kv_f32_kernel|bwd_q_f32_kernel|pattern_bitmap_kernel|pattern_list_kernel|"
+                       r"pattern_layout_full_kernel|fwd_full_merge_kernel|full_sum_kernel|fwd_fp8_kernel|quant_\w+?kernel|"
+                       r"elementwise_kernel|copy\w*)(I\w*?E(?:EvP|Ev$|EEv))?")
+# mask mode (second template argument of the bf16 kernels); the unmasked one is unnamed
+MODE_NAMES = {"1": "window", "2": "pattern", "3": "full"}
 
 
 def short(name):
     m = KERNEL_RE.search(name)
     if not m:
         return name[:60]
-    return m.group(1) + (f"<{m.group(2)}>" if m.group(2) else "")
+    args = re.findall(r"Li(\d+)E", m.group(2) or "")
+    if not args:
+        return m.group(1)
+    label = args[0]
+    if len(args) > 1 and m.group(1).endswith("bf16_kernel") and args[1] in MODE_NAMES:
+        label += "," + MODE_NAMES[args[1]]
+    elif len(args) > 1 and m.group(1) == "full_sum_kernel":
+        label += "," + args[1]
+    return f"{m.group(1)}<{label}>"
 
 
 def stats(path, cmd):

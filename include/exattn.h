@@ -243,9 +243,13 @@ typedef struct {
 
 /*
  * Workspace for attn_fwd_pattern and attn_bwd_pattern: the global-token
- * bitmap, each kernel's per-workgroup tile lists (built on the device by
- * every call, in stream order, before the attention kernels), and the
- * backward's row arrays.  Returns 0 for arguments the calls would reject.
+ * bitmap, the full positions (query rows that see every key: global tokens
+ * and rows whose layout row is set in every block; keys that every row sees,
+ * likewise) with their index lists, each kernel's per-workgroup tile lists
+ * (all built on the device by every call, in stream order, before the
+ * attention kernels), the partial results of the full positions'
+ * pass (B*H slots of 2d floats per quarter of n), and the backward's row
+ * arrays.  Returns 0 for arguments the calls would reject.
  */
 size_t attn_pattern_workspace_bytes(int dtype, int B, int H, int n, int d);
 
@@ -254,7 +258,10 @@ size_t attn_pattern_workspace_bytes(int dtype, int B, int H, int n, int d);
  * attn_bwd (multi-head layout [B, H, n, d]), with the pattern in place of
  * the window.  Only EXATTN_BF16 is supported (EXATTN_EUNSUPPORTED for f32).
  * The workgroups visit only the tiles that hold a visible pair; tiles the
- * pattern covers completely run unmasked.  The backward's O and LSE must
+ * pattern covers completely run unmasked.  Full positions (see above) are
+ * computed by a pass of their own, split over chunks of the other side whose
+ * partial results are merged in a fixed order, so every call is
+ * deterministic.  The backward's O and LSE must
  * come from attn_fwd_pattern with the same pattern.  Besides the errors of
  * attn_fwd / attn_bwd: EXATTN_EINVAL for a NULL descriptor, window < -1,
  * n_global < 0, a NULL or misaligned global_idx with n_global > 0, a NULL

@@ -85,6 +85,54 @@ def test_pattern_parity(name, n, d, window, glob, density):
     print(f"[pattern] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
 
 
+def bigbird_layout(n, n_glob_blocks, density, seed):
+    """Random blocks plus the diagonal, with the first block rows and columns
+    set in every block (their positions are full rows and full keys)."""
+    lay = random_layout(n, density, seed).astype(bool)
+    lay[:n_glob_blocks, :] = True
+    lay[:, :n_glob_blocks] = True
+    return lay.astype(np.uint8)
+
+
+# Full positions (rows that see every key, keys every row sees) go through
+# their own pass: one workgroup per chunk of the other side, chunks merged.
+# n >= 2048 gives several chunks on every pass; many full positions give
+# several workgroups of them and a single chunk.
+FULL_CASES = [
+    # name, n, d, window, globals, layout builder or None
+    ("chunks_globals_d128", 4096, 128, 64, (0, 1, 2000, 4095), None),
+    ("chunks_layout_d128", 4096, 128, -1, (), lambda n: bigbird_layout(n, 2, 0.03, n)),
+    ("chunks_union_d64", 2500, 64, 20, (7, 1234, 2499), lambda n: bigbird_layout(n, 1, 0.05, n)),
+    ("chunks_union_d256", 2112, 256, 30, (100, 2111), lambda n: bigbird_layout(n, 1, 0.05, n)),
+    ("many_full_rows_d128", 3000, 128, 10, tuple(range(0, 3000, 7)), None),
+    ("ragged_tail_global_d128", 2049, 128, 5, (2048,), None),
+]
+
+
+@pytest.mark.parametrize("name,n,d,window,glob,builder", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+def test_pattern_full_positions(name, n, d, window, glob, builder):
+    wl = make_case(1, 2, n, d, "bf16", seed=11 * n + d)
+    print(f"[pattern-full-pos] {name}", flush=True)
+    layout = None if builder is None else builder(n)
+    inputs = draw_inputs(wl)
+    got = run_pattern(wl, inputs, window, glob, layout)
+    ref = oracle_pattern(wl, inputs, window, glob, layout)
+    errs = check_outputs("bf16", got, ref, name)
+    print(f"[pattern-full-pos] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+
+
+def test_pattern_full_positions_repeat_bitwise():
+    # the chunk merge and sums run in a fixed order: two calls agree bit for bit
+    n, d = 4096, 128
+    wl = make_case(1, 2, n, d, "bf16", seed=3)
+    layout = bigbird_layout(n, 2, 0.03, 5)
+    inputs = draw_inputs(wl)
+    a = run_pattern(wl, inputs, 16, (0, 3000), layout)
+    b = run_pattern(wl, inputs, 16, (0, 3000), layout)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
 def test_pattern_empty_rows_follow_the_convention():
     # no window, no globals, a layout whose second block row is empty: rows
     # 64..127 get O = 0, LSE = -inf, dQ = 0; the rest match the oracle.
