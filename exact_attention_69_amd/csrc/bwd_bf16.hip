@@ -238,7 +238,7 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
       uint32_t any_key = 0;  // this lane's key is global, or the layout covers the wave
       if constexpr (PATTERN) {
         const int entry = plist[it];
-        need_mask = entry & 1;
+        need_mask = (entry & 1) && !((entry >> (1 + wave)) & 1);  // the layout covers the wave: no mask
         any_key = (uint32_t)key_global | (uint32_t)((entry >> (1 + wave)) & 1);
         gq = pat.gbits[t] >> (4 * hi);  // BQ = 32: one bitmap word per tile
       }
@@ -486,7 +486,7 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
       }
       if constexpr (PATTERN) {
         const int entry = plist[it];
-        need_mask = entry & 1;
+        need_mask = (entry & 1) && !((entry >> (1 + wave)) & 1);  // the layout covers the wave: no mask
         any_row = (uint32_t)row_global | (uint32_t)((entry >> (1 + wave)) & 1);
       }
 #pragma unroll
@@ -550,34 +550,29 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
 
 // Sum of the full positions' chunks (when there are several), in chunk
 // order: each slot holds NOUT vectors of D floats (dK then dV, or dQ), the
-// sums go to out[0..NOUT) at the position's row, in bf16.  One wave per
-// (head, position), in a grid-stride loop.
+// sums go to out[0..NOUT) at the position's row, in bf16.  One thread per
+// four consecutive elements, in a grid-stride loop.
 template <int D, int NOUT>
 __global__ __launch_bounds__(256) void full_sum_kernel(FullDev full, __bf16* __restrict__ out0,
                                                        __bf16* __restrict__ out1, int n, int heads) {
-  constexpr int PER = D / 64;  // elements per lane
+  constexpr int Q4 = NOUT * D / 4;  // groups of four per slot
   const int R = full.info[kFullCount], C = full.info[kFullChunks];
   if (C <= 1) return;
   const size_t GB = (size_t)full.info[kFullGroups] * kFullRows;  // slots per (head, chunk)
-  const int lane = threadIdx.x & 63;
-  const long nwaves = (long)gridDim.x * (blockDim.x >> 6);
-  const long items = (long)heads * R;
-  for (long it = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); it < items; it += nwaves) {
-    const int head = (int)(it / R), slot = (int)(it - (long)head * R);
-    const size_t s0 = (size_t)head * C * GB + slot;
-    const size_t dst = ((size_t)head * n + full.idx[slot]) * D + lane * PER;
-#pragma unroll
-    for (int k = 0; k < NOUT; ++k) {
-      float acc[PER] = {};
-      for (int c = 0; c < C; ++c) {
-        const float* src = full.part + (s0 + c * GB) * (NOUT * D) + k * D + lane * PER;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += src[i];
-      }
-      __bf16* o = k == 0 ? out0 : out1;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) o[dst + i] = (__bf16)acc[i];
-    }
+  const long items = (long)heads * R * Q4;
+  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (long)gridDim.x * blockDim.x) {
+    const long hs = it / Q4;
+    const int q = (int)(it - hs * Q4);
+    const int head = (int)(hs / R), slot = (int)(hs - (long)head * R);
+    const float* src = full.part + ((size_t)head * C * GB + slot) * (NOUT * D) + 4 * q;
+    const size_t stride = GB * (NOUT * D);
+    f32x4 acc = *(const f32x4*)src;
+    for (int c = 1; c < C; ++c) acc += *(const f32x4*)(src + c * stride);
+    const int k = (4 * q) / D, dd = (4 * q) % D;
+    u32x2 w;
+    w[0] = pack_bf16x2(acc[0], acc[1]);
+    w[1] = pack_bf16x2(acc[2], acc[3]);
+    *(u32x2*)((k == 0 ? out0 : out1) + ((size_t)head * n + full.idx[slot]) * D + dd) = w;
   }
 }
 
@@ -603,7 +598,7 @@ hipError_t bwd_passes(const BwdParams& p, unsigned stages, hipStream_t stream) {
                        p.group, pkv, p.full_kv);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && W == kMaskFull) {
-      hipLaunchKernelGGL((full_sum_kernel<D, 2>), dim3(256), dim3(256), 0, stream, p.full_kv, (__bf16*)p.dk,
+      hipLaunchKernelGGL((full_sum_kernel<D, 2>), dim3(1024), dim3(256), 0, stream, p.full_kv, (__bf16*)p.dk,
                          (__bf16*)p.dv, p.n, (int)kv_heads);
       e = hipGetLastError();
     }
@@ -616,7 +611,7 @@ hipError_t bwd_passes(const BwdParams& p, unsigned stages, hipStream_t stream) {
                        p.full_q);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && W == kMaskFull) {
-      hipLaunchKernelGGL((full_sum_kernel<D, 1>), dim3(256), dim3(256), 0, stream, p.full_q, (__bf16*)p.dq,
+      hipLaunchKernelGGL((full_sum_kernel<D, 1>), dim3(1024), dim3(256), 0, stream, p.full_q, (__bf16*)p.dq,
                          (__bf16*)nullptr, p.n, (int)heads);
       e = hipGetLastError();
     }

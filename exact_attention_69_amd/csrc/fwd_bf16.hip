@@ -271,7 +271,9 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
       }
       if constexpr (PATTERN) {
         const int entry = plist[j];
-        if (entry & 1) {
+        // a wave the layout covers for the whole tile needs no mask unless
+        // the tile crosses the end of the sequence
+        if ((entry & 1) && !(((entry >> (1 + wave)) & 1) && kbase + BC <= n)) {
           static_assert(RB == 1 && BC % 32 == 0, "pattern masks assume one 32-row block per wave");
           // visible: key < n and (band or global row or global key or the
           // layout covers this wave's rows for the tile).  Evaluated with
@@ -431,40 +433,40 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
 // Merge of the full rows' chunks (when there are several): with each
 // chunk's normalised O_c and log-sum-exp L_c, L = log sum_c exp(L_c) and
 // O = sum_c exp(L_c - L) O_c (the two-block merge of the online softmax,
-// applied over all chunks at once).  One wave per (head, full row), in a
-// grid-stride loop; the chunks are read in order, so the result is
-// deterministic.
+// applied over all chunks at once).  One thread per four consecutive
+// elements of a row, in a grid-stride loop; the chunks are read in order, so
+// the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_full_merge_kernel(FullDev full, __bf16* __restrict__ Og,
                                                              float* __restrict__ LSEg, int n, int heads) {
-  constexpr int PER = D / 64;  // elements per lane
+  constexpr int Q4 = D / 4;
   const int R = full.info[kFullCount], C = full.info[kFullChunks];
   if (C <= 1) return;
   const size_t GB = (size_t)full.info[kFullGroups] * kFullRows;  // slots per (head, chunk)
-  const int lane = threadIdx.x & 63;
-  const long nwaves = (long)gridDim.x * (blockDim.x >> 6);
-  const long items = (long)heads * R;
-  for (long it = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); it < items; it += nwaves) {
-    const int head = (int)(it / R), slot = (int)(it - (long)head * R);
+  const long items = (long)heads * R * Q4;
+  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (long)gridDim.x * blockDim.x) {
+    const long hs = it / Q4;
+    const int q = (int)(it - hs * Q4);
+    const int head = (int)(hs / R), slot = (int)(hs - (long)head * R);
     const size_t s0 = (size_t)head * C * GB + slot;
     float m = kNegInf;
     for (int c = 0; c < C; ++c) m = fmaxf(m, full.part_lse[s0 + c * GB]);
-    float acc[PER] = {}, l = 0.0f;
+    f32x4 acc = f32x4{};
+    float l = 0.0f;
     if (m != kNegInf) {
       for (int c = 0; c < C; ++c) {
         const float w = expf(full.part_lse[s0 + c * GB] - m);
-        const float* src = full.part + (s0 + c * GB) * D + lane * PER;
         l += w;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += w * src[i];
+        acc += w * *(const f32x4*)(full.part + (s0 + c * GB) * D + 4 * q);
       }
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const int row = full.idx[slot];
-    __bf16* dst = Og + ((size_t)head * n + row) * D + lane * PER;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) dst[i] = (__bf16)(acc[i] * inv);
-    if (lane == 0) LSEg[(size_t)head * n + row] = l > 0.0f ? m + logf(l) : kNegInf;
+    u32x2 w;
+    w[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    w[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *(u32x2*)(Og + ((size_t)head * n + row) * D + 4 * q) = w;
+    if (q == 0) LSEg[(size_t)head * n + row] = l > 0.0f ? m + logf(l) : kNegInf;
   }
 }
 
@@ -480,7 +482,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
                      nqb, (int)total, scale_log2, p.window, p.group, p.pattern, p.full);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || MODE != kMaskFull) return e;
-  hipLaunchKernelGGL((fwd_full_merge_kernel<D>), dim3(256), dim3(256), 0, stream, p.full, (__bf16*)p.o, p.lse, p.n,
+  hipLaunchKernelGGL((fwd_full_merge_kernel<D>), dim3(1024), dim3(256), 0, stream, p.full, (__bf16*)p.o, p.lse, p.n,
                      p.B * p.H);
   return hipGetLastError();
 }

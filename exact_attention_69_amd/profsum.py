@@ -152,10 +152,83 @@ def traffic(directory, workload_name, copy_mib, cmds):
     return "\n".join(out)
 
 
+# Kernels of the pattern forward call and backward call (the plan kernels run
+# in both and are reported apart).
+_FWD_CALL = ("fwd_bf16_kernel", "fwd_full_merge_kernel")
+_PLAN = ("pattern_bitmap_kernel", "pattern_list_kernel", "pattern_layout_full_kernel")
+
+
+def _sums(path):
+    """{short kernel name: {counter: total over dispatches}}, {kernel: dispatches}."""
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for row in csv.DictReader(open(path)):
+        k = short(row["Kernel_Name"])
+        tot[k][row["Counter_Name"]] += float(row["Counter_Value"])
+        disp[k].add(row["Dispatch_Id"])
+    return tot, {k: len(v) for k, v in disp.items()}
+
+
+def sparse_io(directory, names, copy_mib, lds_kib, cmds):
+    """Per-step HBM bytes and L1->L2 read bytes of the pattern calls for each
+    workload (counter passes under <directory>/<workload>/p1..p3), set beside
+    the block-sparse I/O bound's terms: Z_input (nonzeros of the inputs),
+    Z_QK (visible pairs), M (fast memory, elements)."""
+    import math
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from workloads import draw_pattern, pattern_pair_count, workload
+    M = lds_kib * 1024 // 2  # bf16 elements
+    head = ["| workload | n | random blocks | Z_QK / n^2 | call | Z_input | Z_QK | split point Z_in^2/Z_QK "
+            "(per head) | sum of Z_in^2/M | sum of Z_in sqrt(Z_QK/M) | HBM read+write (MiB) | HBM / compulsory | "
+            "L1->L2 reads (MiB) | L1->L2 / (2 B x sum of Z_in sqrt(Z_QK/M)) | L1->L2 bytes per visible pair |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    rows = []
+    creq = 0.0
+    for name in names:
+        wl = workload(name)
+        window, glob_, layout = draw_pattern(wl)
+        zqk = pattern_pair_count(wl.n, window, glob_, layout) * wl.B * wl.H
+        f, nf = _sums(os.path.join(directory, name, "p1", "run_counter_collection.csv"))
+        w, _ = _sums(os.path.join(directory, name, "p2", "run_counter_collection.csv"))
+        r, _ = _sums(os.path.join(directory, name, "p3", "run_counter_collection.csv"))
+        copy = [k for k in f if "copy" in k.lower()]
+        cf = copy_mib * 1024.0 / f[copy[0]]["FETCH_SIZE"]
+        cw = copy_mib * 1024.0 / w[copy[0]]["WRITE_SIZE"]
+        creq = copy_mib * 2.0**20 / r[copy[0]]["TCP_TCC_READ_REQ_sum"]  # bytes per L1->L2 read request
+        steps = nf.get(next(k for k in nf if k.startswith("fwd_bf16_kernel") and k.endswith("pattern>")), 1)
+        nd = wl.B * wl.H * wl.n * wl.d
+        for call, zin, comp in (("fwd", 3 * nd, (3 * nd + nd) * 2 + wl.B * wl.H * wl.n * 4),
+                                ("bwd", 5 * nd, (5 * nd + 3 * nd) * 2 + 4 * wl.B * wl.H * wl.n * 4)):
+            ks = [k for k in f if k not in copy and not k.startswith(_PLAN) and
+                  (k.startswith(_FWD_CALL) if call == "fwd" else k.startswith(("bwd_", "full_sum")))]
+            hbm = sum(f[k]["FETCH_SIZE"] * cf + w[k]["WRITE_SIZE"] * cw for k in ks) * 1024 / steps
+            l2 = sum(r[k]["TCP_TCC_READ_REQ_sum"] for k in ks) * creq / steps
+            # the bound is per attention problem (one head); summed over the heads
+            bh = wl.B * wl.H
+            zin_h, zqk_h = zin / bh, zqk / bh
+            small = bh * zin_h * math.sqrt(zqk_h / M)
+            large = bh * zin_h**2 / M
+            rows.append(f"| {name} | {wl.n} | {wl.bigbird[2]} | {zqk_h / wl.n**2:.4f} | {call} | "
+                        f"{zin:.3g} | {zqk:.3g} | {zin_h**2 / zqk_h:.3g} | {large:.3g} | {small:.3g} | "
+                        f"{hbm / 2**20:.0f} | {hbm / comp:.2f} | "
+                        f"{l2 / 2**20:.0f} | {l2 / (2 * small):.2f} | {l2 / zqk:.2f} |")
+    return "\n".join(["Commands:", "", "```"] + cmds + ["```", "",
+                      f"M = {lds_kib} KiB of LDS per CU = {M} bf16 elements.  Compulsory HBM bytes: the call's "
+                      "inputs read once and outputs written once (fwd: Q, K, V -> O, LSE; bwd: Q, K, V, O, dO, "
+                      "LSE -> dQ, dK, dV, with D and LSE*log2(e) written and read).  HBM bytes are FETCH_SIZE and "
+                      "WRITE_SIZE scaled by a plain copy of known size; L1->L2 bytes are TCP_TCC_READ_REQ_sum "
+                      f"times the bytes per request of the same copy ({creq:.0f} B).  Per bench step, summed over "
+                      "the call's kernels (plan kernels excluded).  Z_input and Z_QK are totals over the B*H "
+                      "heads; the bound's terms are taken per head and summed.", ""] + head + rows)
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "traffic":
         print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5].split("\n")))
+    elif mode == "sparseio":  # <dir> <workload,workload,...> <copy MiB> <LDS KiB> <commands>
+        print(sparse_io(sys.argv[2], sys.argv[3].split(","), int(sys.argv[4]), int(sys.argv[5]),
+                        sys.argv[6].split("\n")))
     else:
         path, cmd = sys.argv[2], sys.argv[3]
         print(stats(path, cmd) if mode == "stats" else pmc(path, cmd))

@@ -36,6 +36,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "VARIANTS",
+    "SPARSE_IO",
     "workload",
     "round_to_bf16",
     "draw_head",
@@ -120,6 +121,20 @@ VARIANTS = [
 ]
 
 
+# Block-sparse I/O sweep (not benchmarked by default): BigBird layouts whose
+# visible pairs grow with the number of random blocks per block row at a
+# fixed input size, and whose inputs grow with n at a fixed layout density.
+SPARSE_IO = [
+    Workload(f"bf16_b1h16_n16384_d128_bigbird_r{r}", 1, 16, 16384, 128, "bf16", seed=69008, bigbird=(3, 2, r),
+             note=f"BigBird with {r} random blocks per block row")
+    for r in (1, 7, 15)
+] + [
+    Workload(f"bf16_b1h16_n{n}_d128_bigbird_b64", 1, 16, n, 128, "bf16", seed=69008, bigbird=(3, 2, 3),
+             note=f"BigBird 3/2/3 at n={n}")
+    for n in (8192, 32768)
+]
+
+
 def draw_signs(wl, d=None):
     """The +-1 signs of the FP8 rotation (float32, d entries)."""
     d = wl.d if d is None else d
@@ -177,7 +192,7 @@ def workload(name_or_index):
     """Look a workload up by name or by its position in ``WORKLOADS``."""
     if isinstance(name_or_index, int):
         return WORKLOADS[name_or_index]
-    for w in WORKLOADS + VARIANTS:
+    for w in WORKLOADS + VARIANTS + SPARSE_IO:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)
