@@ -241,17 +241,20 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Workspace layout for a pattern problem: [global bitmap][full-row bitmap]
 // [full-key bitmap][layout flags][full-row list][full-key list][split info]
-// [forward lists][key-side lists][query-side lists][partial results]
+// [forward lists][key-side lists][query-side lists][scratch]
 // [D][LSE*log2(e)], each region 256-byte aligned.  Lists hold, per workgroup
 // row of the kernel's grid, one entry per tile of the other side (the most a
-// workgroup can visit) and a count.  The partial results of the full
-// positions take full_part_rows(n) slots per head of 2d floats (forward: d
-// for O, then one log-sum-exp per slot after all the O slots).
+// workgroup can visit) and a count.  The scratch region serves, in stream
+// order, the key-side pass's copies of the full rows (Q and dO [B*H][n][d]
+// bf16, then LSE*log2(e) and D [B*H][n] fp32) and the partial results of the
+// full positions' passes (full_part_rows(n) slots per head of 2d floats;
+// forward: d for O, then one log-sum-exp per slot after all the O slots).
 struct PatternLayout {
   size_t bitmap, flags, idx, info, fwd, kv, q, part, rows, total;
   int fwd_R, fwd_T, fwd_NW, kv_R, kv_T, kv_NW, q_R, q_T, q_NW;
   int fwd_blocks, fwd_tiles, kv_blocks, kv_tiles, q_blocks, q_tiles;
-  size_t part_floats;  // floats of the partial-result region
+  size_t part_floats;   // floats of the partial results
+  size_t gather_bytes;  // bytes of the full rows' copies
   // offsets from the start of the workspace
   size_t off_gbits, off_rowfull, off_colfull, off_flags, off_rowidx, off_colidx, off_info, off_fwd, off_kv, off_q,
       off_part, off_rows;
@@ -272,12 +275,13 @@ PatternLayout pattern_layout(int B, int H, int n, int d) {
   L.bitmap = align256((size_t)exattn::bitmap_words(n) * 4);
   L.flags = align256(2 * nb * 4);
   L.idx = align256((size_t)n * 4);
-  L.info = align256(3 * exattn::kFullInfoInts * 4);
+  L.info = align256((3 * exattn::kFullInfoInts + 2) * 4);  // split info of 3 kernels, then the 2 counts
   L.fwd = align256((size_t)L.fwd_blocks * (L.fwd_tiles + 1) * 4);
   L.kv = align256((size_t)L.kv_blocks * (L.kv_tiles + 1) * 4);
   L.q = align256((size_t)L.q_blocks * (L.q_tiles + 1) * 4);
   L.part_floats = (size_t)B * H * exattn::full_part_rows(n) * 2 * d;
-  L.part = align256(L.part_floats * 4);
+  L.gather_bytes = (size_t)B * H * n * (4 * (size_t)d + 8);
+  L.part = align256(L.part_floats * 4 > L.gather_bytes ? L.part_floats * 4 : L.gather_bytes);
   L.rows = 2 * ws_region_bytes(B, H, n);
   L.off_gbits = 0;
   L.off_rowfull = L.off_gbits + L.bitmap;
@@ -327,6 +331,7 @@ exattn::PlanInput plan_input(const exattn_pattern* pat, int n, void* workspace, 
   in.layout_flags = (int*)(ws + L.off_flags);
   in.row_idx = (int*)(ws + L.off_rowidx);
   in.col_idx = (int*)(ws + L.off_colidx);
+  in.counts = (int*)(ws + L.off_info) + 3 * exattn::kFullInfoInts;
   return in;
 }
 
@@ -345,11 +350,14 @@ hipError_t build_list(const exattn::PlanInput& in, char* base, int R, int T, int
   pl.transposed = transposed;
   pl.tail_partial = tail_partial;
   pl.own_full = transposed ? in.col_full : in.row_full;
+  pl.other_full = transposed ? in.row_full : in.col_full;
   pl.count = (int*)base;
   pl.list = (int*)base + blocks;
   pl.stride = tiles;
   pl.nblocks = blocks;
-  *dev = exattn::PatternDev{in.window, in.gbits, pl.own_full, pl.list, pl.count, tiles};
+  // the other side's full positions: rows for the key-side pass, else keys
+  *dev = exattn::PatternDev{in.window,     pl.own_full, pl.other_full, transposed ? in.row_idx : in.col_idx,
+                            in.counts + (transposed ? 0 : 1), pl.list, pl.count, tiles};
   return exattn::launch_pattern_list(in, pl, s);
 }
 
@@ -397,6 +405,9 @@ int attn_fwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const
   if (e == hipSuccess)
     e = build_list(in, (char*)workspace + L.off_fwd, L.fwd_R, L.fwd_T, L.fwd_NW, L.fwd_blocks, L.fwd_tiles, false,
                    true, &p.pattern, s);
+  // the full keys' copies (scratch region, before the full rows' partial results)
+  p.pattern.gath_a = (const __bf16*)((char*)workspace + L.off_part);
+  p.pattern.gath_b = p.pattern.gath_a + (size_t)B * H * n * d;
   if (e == hipSuccess) e = exattn::launch_fwd_bf16(p, s);
   return from_hip(e);
 }
@@ -441,6 +452,17 @@ int attn_bwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const
                    &p.pattern_kv, s);
   if (e == hipSuccess)
     e = build_list(in, base + L.off_q, L.q_R, L.q_T, L.q_NW, L.q_blocks, L.q_tiles, false, false, &p.pattern_q, s);
+  {  // the other side's copies for each pass (scratch region, before its partial
+     // results); set after build_list, which writes the whole descriptor
+    const size_t rows = (size_t)B * H * n;
+    __bf16* g = (__bf16*)(base + L.off_part);
+    p.pattern_kv.gath_a = g;
+    p.pattern_kv.gath_b = g + rows * d;
+    p.pattern_kv.gath_s0 = (const float*)(g + 2 * rows * d);
+    p.pattern_kv.gath_s1 = p.pattern_kv.gath_s0 + rows;
+    p.pattern_q.gath_a = g;
+    p.pattern_q.gath_b = g + rows * d;
+  }
   if (e == hipSuccess) e = exattn::launch_bwd_bf16(p, exattn::kStageAll, s);
   return from_hip(e);
 }

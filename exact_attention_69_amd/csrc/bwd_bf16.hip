@@ -137,10 +137,14 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
     q_hi = min(n, q_lo + tl * BQ);
   }
   const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
-  // query tiles visited: a contiguous range, or the pattern plan's list
+  // query tiles visited: a contiguous range, or under a pattern the tiles of
+  // gathered full rows (they see every key) followed by the plan's list;
+  // iteration index i < n_gath is gathered tile i.
   const int* plist = PATTERN ? pat.list + (size_t)kblk * pat.stride : nullptr;
-  const int n_tiles = PATTERN ? pat.count[kblk] : t_hi - t_lo;
-  auto tile_at = [&](int i) { return PATTERN ? plist[i] >> kEntryTileShift : t_lo + i; };
+  const int n_full_rows = PATTERN ? pat.other_count[0] : 0;
+  const int n_gath = (n_full_rows + BQ - 1) / BQ;
+  const int n_tiles = PATTERN ? n_gath + pat.count[kblk] : t_hi - t_lo;
+  auto tile_at = [&](int i) { return PATTERN ? plist[i - n_gath] >> kEntryTileShift : t_lo + i; };
   // query rows that see this lane's key through the band (the window is
   // symmetric), within n
   int row_lo = 0, row_hi = n;
@@ -152,30 +156,47 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
       row_hi = row_lo;
   }
   const unsigned row_span = (unsigned)max(row_hi - row_lo, 0);
-  const bool key_global = PATTERN && bit_of(pat.gbits, my_key);
-  // Under a pattern a wave skips the work of a partial query tile where none
-  // of its keys is seen (the layout misses the wave, the band misses its keys
-  // and the tile holds no global row), and of every tile when its keys are
-  // all full keys or past n; loads and barriers stay shared.
+  // Under a pattern a wave skips the work of a partial listed tile where none
+  // of its keys is seen (the layout misses the wave and the band misses its
+  // keys), and of every tile when its keys are all full keys or past n; loads
+  // and barriers stay shared.
   const int kw0 = kb0 + wave * 32;  // first key of this wave
   const bool wave_live = !PATTERN || (kw0 < n && pat.own_full[kw0 >> 5] != ~0u);
 
   // Q and dO tiles, and the LSE*log2(e) and D values of their rows, go
-  // straight from global memory to LDS.  Rows past n are clamped copies of
-  // row n-1 with LSE = +inf, so their probabilities (and dS) are exactly zero
-  // without a per-element test.
+  // straight from global memory to LDS.  Rows past n (past the count of a
+  // gathered tile) are clamped copies of the last row with LSE = +inf, so
+  // their probabilities (and dS) are exactly zero without a per-element test.
   using Tile = TileAsync<D, BQ, NT>;
   static_assert(BQ == 32, "the row-statistics copy maps 64 lanes to 2 x 32 rows");
-  auto load_tile = [&](int t, int qg, int buf) {
-    const int i0 = t * BQ;
-    // first row of the tile in [B*H*n]; B*H*n*D < 2^31 is checked at the ABI
-    const int qrow = (qh0 + qg) * n + i0;
-    Tile::issue(Qg + qrow * D, n - i0, tiles[buf][0], tid);
-    Tile::issue(dOg + qrow * D, n - i0, tiles[buf][1], tid);
-    if (wave == 0) {  // lanes 0-31: LSE*log2(e) of rows i0.., lanes 32-63: D
-      const int i = qrow + min(l32, n - 1 - i0);
-      const void* src = hi ? (const void*)(Dg + i) : i0 + l32 < n ? (const void*)(LSE2g + i) : (const void*)&kPosInf;
-      lds_dma4(src, &rowst[buf][0][0]);
+  auto load_tile = [&](int i, int qg, int buf) {
+    if constexpr (PATTERN) {
+      // gathered tiles read the full rows' copies, laid out like the rows of
+      // a head; `valid` rows of the tile exist
+      const bool g = i < n_gath;
+      const int i0 = g ? i * BQ : tile_at(i) * BQ;
+      const int valid = (g ? n_full_rows : n) - i0;
+      const int qrow = (qh0 + qg) * n + i0;
+      Tile::issue((g ? pat.gath_a : Qg) + qrow * D, valid, tiles[buf][0], tid);
+      Tile::issue((g ? pat.gath_b : dOg) + qrow * D, valid, tiles[buf][1], tid);
+      if (wave == 0) {  // lanes 0-31: LSE*log2(e) of the tile's rows, lanes 32-63: D
+        const int r = qrow + min(l32, valid - 1);
+        const float* ls = g ? pat.gath_s0 : LSE2g;
+        const float* dd = g ? pat.gath_s1 : Dg;
+        const void* src = hi ? (const void*)(dd + r) : l32 < valid ? (const void*)(ls + r) : (const void*)&kPosInf;
+        lds_dma4(src, &rowst[buf][0][0]);
+      }
+    } else {
+      const int i0 = tile_at(i) * BQ;
+      // first row of the tile in [B*H*n]; B*H*n*D < 2^31 is checked at the ABI
+      const int qrow = (qh0 + qg) * n + i0;
+      Tile::issue(Qg + qrow * D, n - i0, tiles[buf][0], tid);
+      Tile::issue(dOg + qrow * D, n - i0, tiles[buf][1], tid);
+      if (wave == 0) {  // lanes 0-31: LSE*log2(e) of rows i0.., lanes 32-63: D
+        const int r = qrow + min(l32, n - 1 - i0);
+        const void* src = hi ? (const void*)(Dg + r) : i0 + l32 < n ? (const void*)(LSE2g + r) : (const void*)&kPosInf;
+        lds_dma4(src, &rowst[buf][0][0]);
+      }
     }
   };
 
@@ -188,32 +209,34 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
 
   // One sweep over the band's query tiles per query head of the group.
   const int steps = n_tiles * group;
-  if (steps > 0) load_tile(tile_at(0), 0, 0);
+  if (steps > 0) load_tile(0, 0, 0);
   wait_all_and_barrier();
 
   int step = 0;
   for (int qg = 0; qg < group; ++qg)
   for (int it = 0; it < n_tiles; ++it, ++step) {
-    const int t = tile_at(it);
+    const bool gathered = PATTERN && it < n_gath;
+    const int t = gathered ? 0 : tile_at(it);
     const int buf = step & 1;
     // prefetch the next tile (the next head's first tile after the last one);
     // its buffer was released by the last barrier
     if (it + 1 < n_tiles)
-      load_tile(tile_at(it + 1), qg, buf ^ 1);
+      load_tile(it + 1, qg, buf ^ 1);
     else if (qg + 1 < group)
-      load_tile(tile_at(0), qg + 1, buf ^ 1);
+      load_tile(0, qg + 1, buf ^ 1);
     const __bf16* Qs = tiles[buf][0];
     const __bf16* dOs = tiles[buf][1];
     const int i0 = t * BQ;
 
     bool act = true;
     if constexpr (PATTERN) {
-      const int entry = plist[it];
       act = wave_live;
-      if (act && (entry & 1)) {
-        const bool lay = (entry >> (1 + wave)) & 1;
-        const bool band = pat.window >= 0 && i0 <= kw0 + 31 + pat.window && kw0 <= i0 + BQ - 1 + pat.window;
-        act = lay || band || pat.gbits[t] != 0u;  // BQ = 32: one bitmap word per tile
+      if (act && !gathered) {
+        const int entry = plist[it - n_gath];
+        if (entry & 1) {
+          const bool lay = (entry >> (1 + wave)) & 1;
+          act = lay || (pat.window >= 0 && i0 <= kw0 + 31 + pat.window && kw0 <= i0 + BQ - 1 + pat.window);
+        }
       }
     }
     if (act) {
@@ -226,21 +249,24 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
       }
 
       // With a window, queries outside this lane's key band get P = 0 (rows
-      // past n already have P = 0 through their LSE).  Under a pattern, a
-      // partial tile keeps the pairs that the band, a global row, a global key
-      // or the layout make visible.
+      // past n already have P = 0 through their LSE, and so do the empty
+      // slots of a gathered tile).  Under a pattern, a partial listed tile
+      // keeps the pairs that the band or the layout make visible, except
+      // those of full rows (they come from the gathered tiles).
       bool need_mask = false;
-      uint32_t gq = 0;  // global bits of the tile's rows, shifted to this lane's half
       if constexpr (WINDOWED) {
         const int k_lo_w = kb0 + wave * 32;
         need_mask = max(i0 + BQ - 1 - k_lo_w, k_lo_w + 31 - i0) > window;
       }
-      uint32_t any_key = 0;  // this lane's key is global, or the layout covers the wave
+      uint32_t lay = 0;  // the layout covers the wave for the tile
+      uint32_t fr = 0;   // full-row bits of the tile's rows, shifted to this lane's half
       if constexpr (PATTERN) {
-        const int entry = plist[it];
-        need_mask = (entry & 1) && !((entry >> (1 + wave)) & 1);  // the layout covers the wave: no mask
-        any_key = (uint32_t)key_global | (uint32_t)((entry >> (1 + wave)) & 1);
-        gq = pat.gbits[t] >> (4 * hi);  // BQ = 32: one bitmap word per tile
+        if (!gathered) {
+          const int entry = plist[it - n_gath];
+          lay = (entry >> (1 + wave)) & 1;
+          need_mask = (entry & 1) && !(lay && !(entry & kEntryHasFull));  // covered by the layout, no full row
+          if (need_mask) fr = pat.other_full[t] >> (4 * hi);  // BQ = 32: one bitmap word per tile
+        }
       }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -254,9 +280,9 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
           // queries that see this lane's key: [row_lo, row_lo + row_span)
           if (WINDOWED && need_mask) p = (unsigned)(i0 + rb + j - row_lo) < row_span ? p : 0.0f;
           if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
-            const uint32_t vis = (uint32_t)((unsigned)(i0 + rb + j - row_lo) < row_span) | any_key |
-                                 ((gq >> (8 * g + j)) & 1u);
-            p = vis ? p : 0.0f;
+            const uint32_t vis = ((uint32_t)((unsigned)(i0 + rb + j - row_lo) < row_span) | lay) &
+                                 ~(fr >> (8 * g + j));
+            p = (vis & 1u) ? p : 0.0f;
           }
           s[r] = p;
           dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
@@ -402,10 +428,14 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
     k_hi = min(n, k_lo + tl * BC);
   }
   const int t_lo = k_lo / BC, t_hi = (k_hi + BC - 1) / BC;
-  // key tiles visited: a contiguous range, or the pattern plan's list
+  // key tiles visited: a contiguous range, or under a pattern the tiles of
+  // gathered full keys (every row sees them) followed by the plan's list;
+  // iteration index i < n_gath is gathered tile i.
   const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
-  const int n_tiles = PATTERN ? pat.count[qb] : t_hi - t_lo;
-  auto tile_at = [&](int i) { return PATTERN ? plist[i] >> kEntryTileShift : t_lo + i; };
+  const int n_full_keys = PATTERN ? pat.other_count[0] : 0;
+  const int n_gath = (n_full_keys + BC - 1) / BC;
+  const int n_tiles = PATTERN ? n_gath + pat.count[qb] : t_hi - t_lo;
+  auto tile_at = [&](int i) { return PATTERN ? plist[i - n_gath] >> kEntryTileShift : t_lo + i; };
   // keys visible to this lane's row through the band
   int key_lo = 0, key_hi = n;
   if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
@@ -416,49 +446,59 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
       key_hi = key_lo;
   }
   const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
-  const bool row_global = PATTERN && bit_of(pat.gbits, my_row);
-  // Under a pattern a wave skips the work of a partial key tile that none of
-  // its rows sees, and of every tile when its rows are all full rows or past n.
+  // Under a pattern a wave skips the work of a partial listed key tile that
+  // none of its rows sees, and of every tile when its rows are all full rows
+  // or past n.
   const int rw0 = q0 + wave * 32;  // first row of this wave
   const bool wave_live = !PATTERN || (rw0 < n && pat.own_full[rw0 >> 5] != ~0u);
 
   // K and V tiles go straight from global memory to LDS.  Key rows past n
   // are zeros in the K tile, so whatever their dS, they add exactly nothing
-  // to dQ = dS K (their V rows are clamped copies and only feed that dS).
+  // to dQ = dS K (their V rows are clamped copies and only feed that dS); the
+  // same holds for the slots of a gathered tile past the full keys' count.
   using Tile = TileAsync<D, BC, NT>;
   using TileK = TileAsyncZeroTail<D, BC, NT>;
-  auto load_tile = [&](int t, int buf) {
-    const int kbase = t * BC;
-    TileK::issue(K + (size_t)kbase * D, n - kbase, tiles[buf][0], tid);
-    Tile::issue(V + (size_t)kbase * D, n - kbase, tiles[buf][1], tid);
+  auto load_tile = [&](int i, int buf) {
+    if constexpr (PATTERN) {
+      // gathered tiles read the full keys' copies, laid out like the rows of
+      // a key/value head
+      const bool g = i < n_gath;
+      const int r0 = g ? i * BC : tile_at(i) * BC;
+      const int valid = (g ? n_full_keys : n) - r0;
+      TileK::issue((g ? pat.gath_a + kv_off : K) + (size_t)r0 * D, valid, tiles[buf][0], tid);
+      Tile::issue((g ? pat.gath_b + kv_off : V) + (size_t)r0 * D, valid, tiles[buf][1], tid);
+    } else {
+      const int kbase = tile_at(i) * BC;
+      TileK::issue(K + (size_t)kbase * D, n - kbase, tiles[buf][0], tid);
+      Tile::issue(V + (size_t)kbase * D, n - kbase, tiles[buf][1], tid);
+    }
   };
 
   f32x16 dq[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
-  if (n_tiles > 0) load_tile(tile_at(0), 0);
+  if (n_tiles > 0) load_tile(0, 0);
   wait_all_and_barrier();
 
   for (int it = 0; it < n_tiles; ++it) {
-    const int t = tile_at(it);
+    const bool gathered = PATTERN && it < n_gath;
+    const int t = gathered ? 0 : tile_at(it);
     const int buf = it & 1;
-    if (it + 1 < n_tiles) load_tile(tile_at(it + 1), buf ^ 1);  // buffer released by the last barrier
+    if (it + 1 < n_tiles) load_tile(it + 1, buf ^ 1);  // buffer released by the last barrier
     const __bf16* Ks = tiles[buf][0];
     const __bf16* Vs = tiles[buf][1];
     const int kbase = t * BC;
 
     bool act = true;
     if constexpr (PATTERN) {
-      const int entry = plist[it];
       act = wave_live;
-      if (act && (entry & 1)) {
-        const bool lay = (entry >> (1 + wave)) & 1;
-        const bool band = pat.window >= 0 && kbase <= rw0 + 31 + pat.window && rw0 <= kbase + BC - 1 + pat.window;
-        uint32_t g = 0u;
-#pragma unroll
-        for (int w = 0; w < BC / 32; ++w) g |= pat.gbits[(kbase >> 5) + w];
-        act = lay || band || g != 0u;
+      if (act && !gathered) {
+        const int entry = plist[it - n_gath];
+        if (entry & 1) {
+          const bool lay = (entry >> (1 + wave)) & 1;
+          act = lay || (pat.window >= 0 && kbase <= rw0 + 31 + pat.window && rw0 <= kbase + BC - 1 + pat.window);
+        }
       }
     }
     if (act) {
@@ -476,18 +516,21 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
       }
 
       // With a window, keys outside this lane's row band get P = 0 (keys past
-      // n meet zero K rows).  Under a pattern, a partial tile keeps the pairs
-      // that the band, a global row, a global key or the layout make visible.
+      // n meet zero K rows).  Under a pattern, a partial listed tile keeps the
+      // pairs that the band or the layout make visible, except those of full
+      // keys (they come from the gathered tiles).
       bool need_mask = false;
-      uint32_t any_row = 0;  // this lane's row is global, or the layout covers the wave
+      uint32_t lay = 0;  // the layout covers the wave for the tile
       if constexpr (WINDOWED) {
         const int r_lo = q0 + wave * 32;
         need_mask = max(r_lo + 31 - kbase, kbase + BC - 1 - r_lo) > window;
       }
       if constexpr (PATTERN) {
-        const int entry = plist[it];
-        need_mask = (entry & 1) && !((entry >> (1 + wave)) & 1);  // the layout covers the wave: no mask
-        any_row = (uint32_t)row_global | (uint32_t)((entry >> (1 + wave)) & 1);
+        if (!gathered) {
+          const int entry = plist[it - n_gath];
+          lay = (entry >> (1 + wave)) & 1;
+          need_mask = (entry & 1) && !(lay && !(entry & kEntryHasFull));  // covered by the layout, no full key
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -501,9 +544,9 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
           if (PATTERN && need_mask) {  // bitwise: one select, no short-circuit branches
             const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
             const int key = kbase + kb * 32 + e + 4 * hi;
-            const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);
-            const uint32_t vis = (uint32_t)((unsigned)(key - key_lo) < key_span) | any_row | ((gk >> e) & 1u);
-            p = vis ? p : 0.0f;
+            const uint32_t fk = pat.other_full[(kbase >> 5) + kb] >> (4 * hi);
+            const uint32_t vis = ((uint32_t)((unsigned)(key - key_lo) < key_span) | lay) & ~(fk >> e);
+            p = (vis & 1u) ? p : 0.0f;
           }
           dp[kb][r] = p * (dp[kb][r] - dl);  // dS^T (unscaled)
         }
@@ -632,7 +675,17 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const bool with_full = W == kMaskPattern && p.full_kv.idx != nullptr;
   for (unsigned side : {unsigned(kStageKV), unsigned(kStageQ)}) {
     if (!(stages & side)) continue;
-    hipError_t e = bwd_passes<D, W>(p, side, stream);
+    hipError_t e = hipSuccess;
+    // under a pattern, first the copies of the other side's full positions
+    // (the scratch region they use is free again once the previous side's
+    // partial results are summed)
+    if (W == kMaskPattern && side == kStageKV)
+      e = launch_pattern_gather(p.pattern_kv, (const __bf16*)p.q, (const __bf16*)p.dout, p.lse2, p.delta, p.B * p.H,
+                                p.n, D, stream);
+    if (W == kMaskPattern && side == kStageQ)
+      e = launch_pattern_gather(p.pattern_q, (const __bf16*)p.k, (const __bf16*)p.v, nullptr, nullptr,
+                                p.B * p.H / p.group, p.n, D, stream);
+    if (e == hipSuccess) e = bwd_passes<D, W>(p, side, stream);
     if (e == hipSuccess && with_full) e = bwd_passes<D, kMaskFull>(p, side, stream);
     if (e != hipSuccess) return e;
   }
@@ -652,7 +705,14 @@ hipError_t bwd_mode(const BwdParams& p, unsigned stages, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stream) {
-  if (p.pattern_kv.list != nullptr) return bwd_mode<kMaskPattern>(p, stages, stream);
+  if (p.pattern_kv.list != nullptr) {
+    for (const PatternDev* q : {&p.pattern_kv, &p.pattern_q})
+      if (q->list == nullptr || q->count == nullptr || q->own_full == nullptr || q->other_full == nullptr ||
+          q->other_idx == nullptr || q->other_count == nullptr || q->gath_a == nullptr || q->gath_b == nullptr)
+        return hipErrorInvalidValue;
+    if (p.pattern_kv.gath_s0 == nullptr || p.pattern_kv.gath_s1 == nullptr) return hipErrorInvalidValue;
+    return bwd_mode<kMaskPattern>(p, stages, stream);
+  }
   return p.window >= 0 ? bwd_mode<kMaskWindow>(p, stages, stream) : bwd_mode<kMaskNone>(p, stages, stream);
 }
 

@@ -159,13 +159,17 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
   }
   const int t_lo = k_lo / BC;
   const int t_hi = (k_hi + BC - 1) / BC;
+  // Under a pattern: first the tiles of gathered full keys (every row sees
+  // them), then the listed tiles.  Iteration index i < n_gath is gathered
+  // tile i; the others are list entry i - n_gath.
   const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
-  const int n_tiles = PATTERN ? pat.count[qb] : t_hi - t_lo;
-  auto tile_at = [&](int i) { return PATTERN ? plist[i] >> kEntryTileShift : t_lo + i; };
+  const int n_full_keys = PATTERN ? pat.other_count[0] : 0;
+  const int n_gath = (n_full_keys + BC - 1) / BC;
+  const int n_tiles = PATTERN ? n_gath + pat.count[qb] : t_hi - t_lo;
+  auto tile_at = [&](int i) { return PATTERN ? plist[i - n_gath] >> kEntryTileShift : t_lo + i; };
   // keys visible to each of this lane's rows through the band
   int key_lo[RB];
   unsigned key_span[RB];
-  bool row_global[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     int lo = 0, hi_k = n;
@@ -175,9 +179,6 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
         band_keys(my_row[rb], my_row[rb] + 1, n, pat.window, &lo, &hi_k);
       else
         hi_k = lo;  // no band term
-      row_global[rb] = bit_of(pat.gbits, my_row[rb]);
-    } else {
-      row_global[rb] = false;
     }
     key_lo[rb] = lo;
     key_span[rb] = (unsigned)max(hi_k - lo, 0);
@@ -217,35 +218,45 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
 
   // Prologue: K and V of the first tile, K of the second.  Key rows past n
   // are clamped copies; their scores are masked to -inf (P = 0).
-  auto issue_k = [&](int t, __bf16* buf) { Tile::issue(K + (size_t)t * BC * D, n - t * BC, buf, tid); };
-  auto issue_v = [&](int t, __bf16* buf) { Tile::issue(V + (size_t)t * BC * D, n - t * BC, buf, tid); };
+  // Gathered tiles read the full keys' copies, laid out like the rows of a
+  // key/value head (rows past their count: clamped copies, masked below).
+  const size_t gath_off = kv_off;
+  auto issue_kv = [&](const __bf16* src, const __bf16* gath, int i, __bf16* buf) {
+    if constexpr (PATTERN) {
+      const bool g = i < n_gath;
+      const int r0 = g ? i * BC : tile_at(i) * BC;
+      Tile::issue((g ? gath + gath_off : src) + (size_t)r0 * D, (g ? n_full_keys : n) - r0, buf, tid);
+    } else {
+      const int t = tile_at(i);
+      Tile::issue(src + (size_t)t * BC * D, n - t * BC, buf, tid);
+    }
+  };
+  auto issue_k = [&](int i, __bf16* buf) { issue_kv(K, pat.gath_a, i, buf); };
+  auto issue_v = [&](int i, __bf16* buf) { issue_kv(V, pat.gath_b, i, buf); };
   if (n_tiles > 0) {
-    issue_k(tile_at(0), kbuf[0]);
-    issue_v(tile_at(0), vbuf[0]);
-    if (n_tiles > 1) issue_k(tile_at(1), kbuf[1]);
+    issue_k(0, kbuf[0]);
+    issue_v(0, vbuf[0]);
+    if (n_tiles > 1) issue_k(1, kbuf[1]);
   }
   wait_all_and_barrier();
 
-  // Under a pattern a wave skips the work of a partial tile where none of its
-  // rows sees a key (the layout misses the wave, the band misses its rows and
-  // the tile holds no global key), and of every tile when its rows are all
-  // full rows or past n; the loads and barriers stay shared by the workgroup.
+  // Under a pattern a wave skips the work of a partial listed tile where
+  // none of its rows sees a key (the layout misses the wave and the band
+  // misses its rows), and of every tile when its rows are all full rows or
+  // past n; the loads and barriers stay shared by the workgroup.
   bool wave_live = true;
   if constexpr (PATTERN) wave_live = w0 < n && pat.own_full[w0 >> 5] != ~0u;
   auto wave_sees = [&](int i) -> bool {
     if constexpr (!PATTERN) {
       return true;
     } else {
-      const int entry = plist[i];
       if (!wave_live) return false;
+      if (i < n_gath) return true;
+      const int entry = plist[i - n_gath];
       if (!(entry & 1)) return true;
       const int c0 = (entry >> kEntryTileShift) * BC;
-      bool a = (entry >> (1 + wave)) & 1;
-      if (pat.window >= 0) a = a || (c0 <= w0 + 31 + pat.window && w0 <= c0 + BC - 1 + pat.window);
-      uint32_t g = 0u;
-#pragma unroll
-      for (int w = 0; w < BC / 32; ++w) g |= pat.gbits[(c0 >> 5) + w];
-      return a || g != 0u;
+      const bool a = (entry >> (1 + wave)) & 1;
+      return a || (pat.window >= 0 && c0 <= w0 + 31 + pat.window && w0 <= c0 + BC - 1 + pat.window);
     }
   };
 
@@ -254,12 +265,12 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
   if (act_cur) compute_s(kbuf[0], s_cur);
 
   for (int j = 0; j < n_tiles; ++j) {
-    const int t = tile_at(j);
     // V of tile j+1 into the V buffer read last iteration, K of tile j+2 into
     // the K buffer read last iteration (both released by the last barrier).
-    if (j + 1 < n_tiles) issue_v(tile_at(j + 1), vbuf[(j + 1) & 1]);
-    if (j + 2 < n_tiles) issue_k(tile_at(j + 2), kbuf[j & 1]);
-    const int kbase = t * BC;
+    if (j + 1 < n_tiles) issue_v(j + 1, vbuf[(j + 1) & 1]);
+    if (j + 2 < n_tiles) issue_k(j + 2, kbuf[j & 1]);
+    const bool gathered = PATTERN && j < n_gath;
+    const int kbase = gathered ? 0 : tile_at(j) * BC;
 
     const bool act_next = !PATTERN || (j + 1 < n_tiles && wave_sees(j + 1));
     if (act_cur) {
@@ -270,26 +281,35 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
         need_mask = need_mask || max(r_hi - kbase, kbase + BC - 1 - w0) > window;
       }
       if constexpr (PATTERN) {
-        const int entry = plist[j];
-        // a wave the layout covers for the whole tile needs no mask unless
-        // the tile crosses the end of the sequence
-        if ((entry & 1) && !(((entry >> (1 + wave)) & 1) && kbase + BC <= n)) {
-          static_assert(RB == 1 && BC % 32 == 0, "pattern masks assume one 32-row block per wave");
-          // visible: key < n and (band or global row or global key or the
-          // layout covers this wave's rows for the tile).  Evaluated with
+        static_assert(RB == 1 && BC % 32 == 0, "pattern masks assume one 32-row block per wave");
+        // A gathered tile masks only its slots past the full keys' count (its
+        // keys are slots 0.., every row sees them); a listed tile keeps the
+        // pairs of its band or layout that are not full keys (those come from
+        // the gathered tiles), and a wave the layout covers needs no mask
+        // unless the tile crosses the end of the sequence or holds a full key.
+        uint32_t lay = 1u;
+        int key_end = n_full_keys - j * BC;
+        bool mask = key_end < BC;
+        if (!gathered) {
+          const int entry = plist[j - n_gath];
+          lay = (entry >> (1 + wave)) & 1;
+          key_end = n;
+          mask = (entry & 1) && !(lay && kbase + BC <= n && !(entry & kEntryHasFull));
+        }
+        if (mask) {
+          // visible: key < key_end, (band or layout), and not a full key;
           // bitwise operators into one select per element: no short-circuit
-          // branches.
-          const uint32_t any_row = (uint32_t)row_global[0] | (uint32_t)((entry >> (1 + wave)) & 1);
+          // branches
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
-            const uint32_t gk = pat.gbits[(kbase >> 5) + kb] >> (4 * hi);  // keys kbase+32kb+4hi+..
+            const uint32_t fk = gathered ? 0u : pat.other_full[(kbase >> 5) + kb] >> (4 * hi);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int e = 8 * (r >> 2) + (r & 3);  // acc_row(r, lane) - 4*hi
               const int key = kbase + kb * 32 + e + 4 * hi;
-              const uint32_t vis = (uint32_t)(key < n) &
-                                   ((uint32_t)((unsigned)(key - key_lo[0]) < key_span[0]) | any_row | ((gk >> e) & 1u));
-              s_cur[0][kb][r] = vis ? s_cur[0][kb][r] : kNegInf;
+              const uint32_t vis = (uint32_t)(key < key_end) &
+                                   ((uint32_t)((unsigned)(key - key_lo[0]) < key_span[0]) | lay) & ~(fk >> e);
+              s_cur[0][kb][r] = (vis & 1u) ? s_cur[0][kb][r] : kNegInf;
             }
           }
         }
@@ -501,7 +521,13 @@ hipError_t launch_mode(const FwdParams& p, hipStream_t stream) {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   if (p.pattern.list != nullptr) {
-    const hipError_t e = launch_mode<kMaskPattern>(p, stream);
+    if (p.pattern.own_full == nullptr || p.pattern.other_full == nullptr || p.pattern.count == nullptr)
+      return hipErrorInvalidValue;
+    // the full keys' copies, then the pattern pass, then the full rows' pass
+    // (its partial results reuse the copies' scratch region)
+    hipError_t e = launch_pattern_gather(p.pattern, (const __bf16*)p.k, (const __bf16*)p.v, nullptr, nullptr,
+                                         p.B * p.H / p.group, p.n, p.d, stream);
+    if (e == hipSuccess) e = launch_mode<kMaskPattern>(p, stream);
     if (e != hipSuccess || p.full.idx == nullptr) return e;
     return launch_mode<kMaskFull>(p, stream);
   }

@@ -6,15 +6,21 @@
 //   or layout[i / 64][j / 64] is set.
 //
 // A plan step turns the pattern into, for every workgroup of a kernel, the
-// list of tiles it must visit for the positions it stores (full positions,
-// below, are left to a pass of their own).  Each entry is
-//   bits 9..31  tile index
+// list of tiles it must visit for the positions it stores.  Full positions
+// (below) are left out on both sides: the workgroup's own are written by a
+// pass of their own, and those of the other side are gathered into tiles that
+// every workgroup visits before its list, so a listed tile only serves band
+// and layout pairs.  Each entry is
+//   bits 10..31 tile index
+//   bit  9      the tile holds a full position of the other side (masked
+//               out of it)
 //   bits 1..8   per wave: the layout covers this wave's 32 rows (or keys)
 //               for the whole tile
-//   bit  0      partial: some pair of the tile is not visible (or the tile
-//               crosses the end of the sequence), so the kernel applies the
-//               element mask; otherwise every pair is visible.
-// Tiles with no visible pair are not listed.
+//   bit  0      partial: some pair of the tile is not visible, or the tile
+//               holds a full position of the other side, or it crosses the
+//               end of the sequence, so the kernel applies the element mask;
+//               otherwise every pair is visible.
+// Tiles with no band or layout pair of a stored position are not listed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,7 +29,8 @@
 namespace exattn {
 
 constexpr int kLayoutBlock = 64;
-constexpr int kEntryTileShift = 9;
+constexpr int kEntryTileShift = 10;
+constexpr int kEntryHasFull = 1 << 9;
 // Extra zero words after the bitmap, so that reads for rows or keys of a
 // workgroup that runs past the end of the sequence stay in the allocation.
 constexpr int kBitmapPadWords = 16;
@@ -32,14 +39,26 @@ __host__ __device__ inline int bitmap_words(int n) { return (n + 31) / 32 + kBit
 
 // What a kernel needs at run time.
 struct PatternDev {
-  int window;                // -1: no band term
-  const uint32_t* gbits;     // global-token bitmap (bitmap_words(n) words)
-  const uint32_t* own_full;  // full positions of the side a workgroup owns
-                             // (rows, or keys for the key-side pass): not
-                             // stored, the full-position pass writes them
-  const int* list;           // entries, `stride` per workgroup row of the grid
-  const int* count;          // number of entries per workgroup row
+  int window;                  // -1: no band term
+  const uint32_t* own_full;    // full positions of the side a workgroup owns
+                               // (rows, or keys for the key-side pass): not
+                               // stored, the full-position pass writes them
+  const uint32_t* other_full;  // full positions of the other side: visited
+                               // first, gathered into tiles of their own, and
+                               // masked out of the listed tiles
+  const int* other_idx;        // those positions, ascending
+  const int* other_count;      // their number (one int)
+  const int* list;             // entries, `stride` per workgroup row of the grid
+  const int* count;            // number of entries per workgroup row
   int stride;
+  // The other side's full positions copied to slots [head][0, count) (head
+  // stride n rows), so that a gathered tile loads like a contiguous one:
+  // key-side pass: the full rows' Q, dO (a, b), LSE*log2(e) and D (s0, s1);
+  // forward and query-side pass: the full keys' K, V (a, b).
+  const __bf16* gath_a;
+  const __bf16* gath_b;
+  const float* gath_s0;
+  const float* gath_s1;
 };
 
 // Full positions: a query row that sees every key (a global token, or a row
@@ -82,7 +101,8 @@ struct PlanList {
   int R, T, NW;
   bool transposed;
   bool tail_partial;
-  const uint32_t* own_full;  // full positions of the owned side: they drive no tile
+  const uint32_t* own_full;    // full positions of the owned side: they drive no tile
+  const uint32_t* other_full;  // full positions of the other side: gathered, not listed
   int* list;
   int* count;
   int stride;
@@ -102,6 +122,7 @@ struct PlanInput {
   int* layout_flags;            // [layout_n] rows set in every block, [layout_n] columns
   int* row_idx;                 // full rows, ascending (n ints)
   int* col_idx;                 // full keys, ascending (n ints)
+  int* counts;                  // [0] full rows, [1] full keys
 };
 
 // How one consumer kernel splits its full positions: `tiles` tiles of the
@@ -114,6 +135,11 @@ struct FullSplit {
 
 hipError_t launch_pattern_bitmap(const PlanInput& in, const FullSplit* splits, int n_splits, hipStream_t stream);
 hipError_t launch_pattern_list(const PlanInput& in, const PlanList& pl, hipStream_t stream);
+// Copies the other side's full positions of every head into the gather
+// slots of `pat`: rows of a and b (bf16, d wide) and, when s0 is not null,
+// the values of s0 and s1 (heads of n rows each).
+hipError_t launch_pattern_gather(const PatternDev& pat, const __bf16* a, const __bf16* b, const float* s0,
+                                 const float* s1, int heads, int n, int d, hipStream_t stream);
 
 // Element visibility on a partial tile, given the per-row and per-key terms.
 __device__ __forceinline__ bool bit_of(const uint32_t* bits, int pos) { return (bits[pos >> 5] >> (pos & 31)) & 1u; }

@@ -103,6 +103,8 @@ __global__ __launch_bounds__(1024) void pattern_bitmap_kernel(PlanInput in, Full
   write_positions(in.row_full, w0, w1, in.row_idx, pr);
   write_positions(in.col_full, w0, w1, in.col_idx, pc);
   if (tid == 0) {
+    in.counts[0] = rows_total;
+    in.counts[1] = cols_total;
     for (int i = 0; i < sp.count; ++i) {
       const FullSplit& f = sp.s[i];
       const int R = f.keys ? cols_total : rows_total;
@@ -146,7 +148,6 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
   const int n = in.n;
   const int r0 = blk * pl.R, r1 = min(n, r0 + pl.R);  // own positions
   const int n_own = r1 - r0;
-  const int g_own = count_bits(in.gbits, r0, r1);
   // Full own positions are written by the full-position pass: they list no
   // tile, and a block holding only such positions lists none.
   const bool any_part = n_own > count_bits(pl.own_full, r0, r1);
@@ -158,8 +159,9 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
     int entry = -1;
     if (t < ntile) {
       const int c0 = t * pl.T, c1 = min(n, c0 + pl.T);
-      const int n_other = c1 - c0;
-      const int g_other = count_bits(in.gbits, c0, c1);
+      // full positions of the other side are gathered apart: a tile made of
+      // them only is not listed, and one holding any of them is partial
+      const int f_other = count_bits(pl.other_full, c0, c1);
       // queries [q0, q1) against keys [k0, k1)
       const int q0 = pl.transposed ? c0 : r0, q1 = pl.transposed ? c1 : r1;
       const int k0 = pl.transposed ? r0 : c0, k1 = pl.transposed ? r1 : c1;
@@ -168,8 +170,6 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
         any_band = k0 <= q1 - 1 + in.window && q0 <= k1 - 1 + in.window;
         full_band = max(q1 - 1 - k0, k1 - 1 - q0) <= in.window;
       }
-      const int gq = pl.transposed ? g_other : g_own, nq = pl.transposed ? n_other : n_own;
-      const int gk = pl.transposed ? g_own : g_other, nk = pl.transposed ? n_own : n_other;
       // layout bit of each wave's 32 own positions against this tile
       unsigned wbits = 0;
       bool lay_any = false, lay_all = in.layout != nullptr;
@@ -188,12 +188,12 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
           lay_all = lay_all && on;
         }
       }
-      // global positions on the owned side are full positions: only the
-      // other side's global term lists a tile
-      if (any_band || g_other > 0 || lay_any) {
-        const bool full = full_band || gq == nq || gk == nk || lay_all;
+      // Global positions are full positions on either side: only the band
+      // and the layout list a tile.
+      if ((any_band || lay_any) && f_other < c1 - c0) {
+        const bool full = (full_band || lay_all) && f_other == 0;
         const bool partial = !full || (pl.tail_partial && c1 - c0 < pl.T);
-        entry = (t << kEntryTileShift) | (int)(wbits << 1) | (partial ? 1 : 0);
+        entry = (t << kEntryTileShift) | (f_other > 0 ? kEntryHasFull : 0) | (int)(wbits << 1) | (partial ? 1 : 0);
       }
     }
     // compaction: rank among the listed tiles of this chunk, in tile order
@@ -210,7 +210,42 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
   if (tid == 0) pl.count[blk] = total;
 }
 
+// Gather of the other side's full positions: one thread per 16 bytes of a
+// row of a or b (and the row's two values), in a grid-stride loop over
+// heads * count rows.
+__global__ __launch_bounds__(256) void pattern_gather_kernel(PatternDev pat, const __bf16* __restrict__ a,
+                                                             const __bf16* __restrict__ b,
+                                                             const float* __restrict__ s0,
+                                                             const float* __restrict__ s1, int heads, int n, int d) {
+  const int R = pat.other_count[0];
+  const int cpr = d / 8;  // 16-byte chunks per row
+  const long items = (long)heads * R * cpr;
+  __bf16* ga = const_cast<__bf16*>(pat.gath_a);
+  __bf16* gb = const_cast<__bf16*>(pat.gath_b);
+  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (long)gridDim.x * blockDim.x) {
+    const long hs = it / cpr;
+    const int c = (int)(it - hs * cpr);
+    const int head = (int)(hs / R), slot = (int)(hs - (long)head * R);
+    const size_t src = (size_t)head * n + pat.other_idx[slot], dst = (size_t)head * n + slot;
+    *(uint4*)(ga + dst * d + 8 * c) = *(const uint4*)(a + src * d + 8 * c);
+    *(uint4*)(gb + dst * d + 8 * c) = *(const uint4*)(b + src * d + 8 * c);
+    if (s0 != nullptr && c == 0) {
+      const_cast<float*>(pat.gath_s0)[dst] = s0[src];
+      const_cast<float*>(pat.gath_s1)[dst] = s1[src];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pattern_gather(const PatternDev& pat, const __bf16* a, const __bf16* b, const float* s0,
+                                 const float* s1, int heads, int n, int d, hipStream_t stream) {
+  if (pat.other_idx == nullptr || pat.other_count == nullptr || pat.gath_a == nullptr || pat.gath_b == nullptr ||
+      (s0 != nullptr && (s1 == nullptr || pat.gath_s0 == nullptr || pat.gath_s1 == nullptr)))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pattern_gather_kernel, dim3(1024), dim3(256), 0, stream, pat, a, b, s0, s1, heads, n, d);
+  return hipGetLastError();
+}
 
 hipError_t launch_pattern_bitmap(const PlanInput& in, const FullSplit* splits, int n_splits, hipStream_t stream) {
   if (n_splits < 0 || n_splits > 3) return hipErrorInvalidValue;
