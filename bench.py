@@ -22,6 +22,7 @@ the counters' scale for a transfer of known size.
 """
 
 import argparse
+import statistics
 import json
 import os
 import sys
@@ -207,6 +208,7 @@ def time_steps(wl, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     kms = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(nk)]
+    time_steps.last_step_ms = [e[0].elapsed_time(e[nk]) for e in ev]  # per step, for medians
     return names, kms, start.elapsed_time(end) / steps, wall
 
 
@@ -219,6 +221,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration timings of the other workloads")
     ap.add_argument("--variant-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args(argv)
@@ -232,6 +236,7 @@ def main(argv=None):
     wl = workload(args.workload)
     fwd_f, bwd_f = flops(wl)
     names, kms, ms, wall = time_steps(wl, args.steps, args.warmup)
+    main_step_ms = list(time_steps.last_step_ms)
     nk = len(kms)
     fwd_ms = kms[0]
     bwd_ms = sum(kms[1:])
@@ -275,6 +280,30 @@ def main(argv=None):
             entry["hbm_gbs_algorithmic"] = round(sum(hbm_bytes(vw)) / (vms * 1e-3) / 1e9, 1)
             variants[vw.name] = entry
 
+    # Every workload shape: forward, backward and whole-step times (events;
+    # per-kernel means, step median over >= 20 steps, 5 at n >= 32768, after
+    # 5 warm-up steps) and TFLOP/s on the counted FLOPs.
+    configs = {}
+    if not args.no_configs:
+        from workloads import WORKLOADS
+        for cw in WORKLOADS:
+            if cw.name == wl.name:
+                cn, ck, cms, per = names, kms, ms, main_step_ms
+            else:
+                cn, ck, cms, _ = time_steps(cw, 5 if cw.n >= 32768 else 20, 5)
+                per = list(time_steps.last_step_ms)
+            cf, cb = flops(cw)
+            med = statistics.median(per)
+            cpeak = PEAK_TFLOPS[cw.dtype]
+            configs[cw.name] = {
+                "dtype": cw.dtype, "B": cw.B, "H": cw.H, "n": cw.n, "d": cw.d, "window": cw.window,
+                "steps": len(per), "fwd_ms": round(ck[0], 4), "bwd_ms": round(sum(ck[1:]), 4),
+                "step_ms_median": round(med, 4), "fwd_tflops": round(cf / (ck[0] * 1e-3) / 1e12, 2),
+                "bwd_tflops": round(cb / (sum(ck[1:]) * 1e-3) / 1e12, 2),
+                "tflops": round((cf + cb) / (med * 1e-3) / 1e12, 2), "peak_tflops": cpeak,
+                "pct_peak": round(100.0 * (cf + cb) / (med * 1e-3) / 1e12 / cpeak, 2),
+                "kernel_ms": {cn[i]: round(ck[i], 4) for i in range(len(cn))}}
+
     if args.copy_calibration:
         import torch
         dev = torch.device("cuda:0")
@@ -304,6 +333,8 @@ def main(argv=None):
     }
     if variants:
         out["variants"] = variants
+    if configs:
+        out["configs"] = configs
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
