@@ -143,7 +143,8 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
   const int* plist = PATTERN ? pat.list + (size_t)kblk * pat.stride : nullptr;
   const int n_full_rows = PATTERN ? pat.other_count[0] : 0;
   const int n_gath = (n_full_rows + BQ - 1) / BQ;
-  const int n_tiles = PATTERN ? n_gath + pat.count[kblk] : t_hi - t_lo;
+  const int n_listed = PATTERN ? pat.count[kblk] : 0;
+  const int n_tiles = PATTERN ? (n_listed < 0 ? 0 : n_gath + n_listed) : t_hi - t_lo;
   auto tile_at = [&](int i) { return PATTERN ? plist[i - n_gath] >> kEntryTileShift : t_lo + i; };
   // query rows that see this lane's key through the band (the window is
   // symmetric), within n
@@ -434,7 +435,8 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
   const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
   const int n_full_keys = PATTERN ? pat.other_count[0] : 0;
   const int n_gath = (n_full_keys + BC - 1) / BC;
-  const int n_tiles = PATTERN ? n_gath + pat.count[qb] : t_hi - t_lo;
+  const int n_listed = PATTERN ? pat.count[qb] : 0;
+  const int n_tiles = PATTERN ? (n_listed < 0 ? 0 : n_gath + n_listed) : t_hi - t_lo;
   auto tile_at = [&](int i) { return PATTERN ? plist[i - n_gath] >> kEntryTileShift : t_lo + i; };
   // keys visible to this lane's row through the band
   int key_lo = 0, key_hi = n;

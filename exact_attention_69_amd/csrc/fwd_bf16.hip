@@ -165,7 +165,8 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void f
   const int* plist = PATTERN ? pat.list + (size_t)qb * pat.stride : nullptr;
   const int n_full_keys = PATTERN ? pat.other_count[0] : 0;
   const int n_gath = (n_full_keys + BC - 1) / BC;
-  const int n_tiles = PATTERN ? n_gath + pat.count[qb] : t_hi - t_lo;
+  const int n_listed = PATTERN ? pat.count[qb] : 0;
+  const int n_tiles = PATTERN ? (n_listed < 0 ? 0 : n_gath + n_listed) : t_hi - t_lo;
   auto tile_at = [&](int i) { return PATTERN ? plist[i - n_gath] >> kEntryTileShift : t_lo + i; };
   // keys visible to each of this lane's rows through the band
   int key_lo[RB];

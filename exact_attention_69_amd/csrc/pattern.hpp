@@ -49,7 +49,8 @@ struct PatternDev {
   const int* other_idx;        // those positions, ascending
   const int* other_count;      // their number (one int)
   const int* list;             // entries, `stride` per workgroup row of the grid
-  const int* count;            // number of entries per workgroup row
+  const int* count;            // number of entries per workgroup row (-1: the
+                               // row's own positions are all full: no work)
   int stride;
   // The other side's full positions copied to slots [head][0, count) (head
   // stride n rows), so that a gathered tile loads like a contiguous one:

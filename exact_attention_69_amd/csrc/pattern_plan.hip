@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanLis
     total += wave_count[0] + wave_count[1] + wave_count[2] + wave_count[3];
     __syncthreads();  // wave_count is rewritten by the next chunk
   }
-  if (tid == 0) pl.count[blk] = total;
+  if (tid == 0) pl.count[blk] = any_part ? total : -1;  // -1: every own position is full, nothing to do
 }
 
 // Gather of the other side's full positions: one thread per 16 bytes of a

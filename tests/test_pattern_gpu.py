@@ -133,6 +133,71 @@ def test_pattern_full_positions_repeat_bitwise():
         assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
+def test_pattern_duplicate_and_out_of_range_globals():
+    # global_idx may repeat positions and hold positions outside [0, n): the
+    # pattern is that of the distinct positions inside
+    n, d = 700, 128
+    wl = make_case(1, 2, n, d, "bf16", seed=21)
+    raw = (5, 5, -3, 17, n, n + 100, 17, 640)
+    inputs = draw_inputs(wl)
+    got = run_pattern(wl, inputs, 9, raw, None)
+    ref = oracle_pattern(wl, inputs, 9, (5, 17, 640), None)
+    check_outputs("bf16", got, ref, "dup_globals")
+
+
+@pytest.mark.parametrize("n", [1, 2, 33])
+def test_pattern_tiny(n):
+    wl = make_case(1, 2, n, 64, "bf16", seed=40 + n)
+    inputs = draw_inputs(wl)
+    for window, glob in ((0, ()), (-1, (0,)), (1, (n - 1,))):
+        got = run_pattern(wl, inputs, window, glob, None)
+        ref = oracle_pattern(wl, inputs, window, glob, None)
+        check_outputs("bf16", got, ref, f"tiny n={n} w={window} g={glob}")
+
+
+def test_pattern_all_rows_empty():
+    # an empty layout, no window, no globals: every row sees nothing
+    n, d = 300, 128
+    wl = make_case(1, 2, n, d, "bf16", seed=8)
+    layout = np.zeros((-(-n // 64),) * 2, dtype=np.uint8)
+    got = run_pattern(wl, draw_inputs(wl), -1, (), layout)
+    assert np.all(got["o"] == 0.0) and np.all(np.isneginf(got["lse"]))
+    for k in ("dq", "dk", "dv"):
+        assert np.all(got[k] == 0.0), k
+
+
+def test_pattern_full_layout_is_dense_attention():
+    # every block set: every row and key is a full position; the pattern
+    # passes have nothing to do and the full-position passes compute it all
+    import torch
+    import exact_attention_69_amd as ea
+    n, d = 1000, 128
+    wl = make_case(1, 2, n, d, "bf16", seed=9)
+    inputs = draw_inputs(wl)
+    layout = np.ones((-(-n // 64),) * 2, dtype=np.uint8)
+    got = run_pattern(wl, inputs, -1, (), layout)
+    ref = oracle_pattern(wl, inputs, -1, (), layout)
+    check_outputs("bf16", got, ref, "full_layout")
+    t = to_device(inputs, "bf16")
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale, -1)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(got["lse"], lse.cpu().numpy(), atol=1e-4, rtol=1e-5)
+
+
+def test_pattern_window_covering_everything_is_dense_attention():
+    import torch
+    import exact_attention_69_amd as ea
+    n, d = 800, 64
+    wl = make_case(1, 2, n, d, "bf16", seed=10)
+    inputs = draw_inputs(wl)
+    got = run_pattern(wl, inputs, n, (3,), None)
+    t = to_device(inputs, "bf16")
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale, -1)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(got["o"], o.float().cpu().numpy(), atol=2e-2, rtol=0)
+    np.testing.assert_allclose(got["lse"], lse.cpu().numpy(), atol=1e-4, rtol=1e-5)
+
+
 def test_pattern_empty_rows_follow_the_convention():
     # no window, no globals, a layout whose second block row is empty: rows
     # 64..127 get O = 0, LSE = -inf, dQ = 0; the rest match the oracle.
