@@ -36,10 +36,11 @@ struct KvCfg {
   static constexpr int WPE = D == 256 ? 1 : 2;  // waves per SIMD
 };
 
-// Waves per workgroup: the full-key pass gathers kFullRows keys.
+// Waves per workgroup: the full-key pass gathers kFullRows keys; 4 under a
+// pattern (as in the forward).
 template <int D, int MODE>
 constexpr int kv_waves() {
-  return MODE == kMaskFull ? kFullRows / 32 : KvCfg<D>::NW;
+  return MODE == kMaskFull ? kFullRows / 32 : MODE == kMaskPattern ? 4 : KvCfg<D>::NW;
 }
 
 // This workgroup's item of a full-position launch: (head, chunk, group of
@@ -359,7 +360,7 @@ struct QCfg<256> {
 
 template <int D, int MODE>
 constexpr int q_waves() {
-  return MODE == kMaskFull ? kFullRows / 32 : QCfg<D>::NW;
+  return MODE == kMaskFull ? kFullRows / 32 : MODE == kMaskPattern ? 4 : QCfg<D>::NW;
 }
 
 // MODE as for the key side, with query rows owned: kMaskFull gathers a
@@ -719,18 +720,19 @@ hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stre
 }
 
 void bwd_kv_bf16_geometry(int d, int* keys_per_block, int* rows_per_tile, int* waves) {
-  const int nw = d == 64 ? KvCfg<64>::NW : d == 128 ? KvCfg<128>::NW : KvCfg<256>::NW;
-  *keys_per_block = 32 * nw;
+  *waves = d == 64 ? kv_waves<64, kMaskPattern>() : d == 128 ? kv_waves<128, kMaskPattern>()
+                                                             : kv_waves<256, kMaskPattern>();
+  *keys_per_block = 32 * *waves;
   *rows_per_tile = KvCfg<128>::BQ;
-  *waves = nw;
 }
 
 void bwd_q_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves) {
   switch (d) {
-    case 64: *rows_per_block = 32 * QCfg<64>::NW; *keys_per_tile = QCfg<64>::BC; *waves = QCfg<64>::NW; break;
-    case 128: *rows_per_block = 32 * QCfg<128>::NW; *keys_per_tile = QCfg<128>::BC; *waves = QCfg<128>::NW; break;
-    default: *rows_per_block = 32 * QCfg<256>::NW; *keys_per_tile = QCfg<256>::BC; *waves = QCfg<256>::NW; break;
+    case 64: *keys_per_tile = QCfg<64>::BC; *waves = q_waves<64, kMaskPattern>(); break;
+    case 128: *keys_per_tile = QCfg<128>::BC; *waves = q_waves<128, kMaskPattern>(); break;
+    default: *keys_per_tile = QCfg<256>::BC; *waves = q_waves<256, kMaskPattern>(); break;
   }
+  *rows_per_block = 32 * *waves;
 }
 
 }  // namespace exattn

@@ -57,10 +57,13 @@ struct FwdCfg<256> {
   static constexpr int NW = 4, RB = 1, BC = 32, WPE = 1;
 };
 
-// Waves per workgroup: the full-row pass gathers kFullRows rows.
+// Waves per workgroup: the full-row pass gathers kFullRows rows; under a
+// pattern, 4 waves: a partial tile often keeps only some waves busy, and two
+// 4-wave workgroups per CU fill each other's idle SIMDs (8 waves were 14-26%
+// slower on the Longformer and BigBird workloads).
 template <int D, int MODE>
 constexpr int fwd_waves() {
-  return MODE == kMaskFull ? kFullRows / 32 : FwdCfg<D>::NW;
+  return MODE == kMaskFull ? kFullRows / 32 : MODE == kMaskPattern ? 4 : FwdCfg<D>::NW;
 }
 
 // MODE: kMaskNone, kMaskWindow (contiguous band of key tiles, analytic
@@ -537,10 +540,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
 
 void fwd_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves) {
   switch (d) {
-    case 64: *rows_per_block = 32 * FwdCfg<64>::NW; *keys_per_tile = FwdCfg<64>::BC; *waves = FwdCfg<64>::NW; break;
-    case 128: *rows_per_block = 32 * FwdCfg<128>::NW; *keys_per_tile = FwdCfg<128>::BC; *waves = FwdCfg<128>::NW; break;
-    default: *rows_per_block = 32 * FwdCfg<256>::NW; *keys_per_tile = FwdCfg<256>::BC; *waves = FwdCfg<256>::NW; break;
+    case 64: *keys_per_tile = FwdCfg<64>::BC; *waves = fwd_waves<64, kMaskPattern>(); break;
+    case 128: *keys_per_tile = FwdCfg<128>::BC; *waves = fwd_waves<128, kMaskPattern>(); break;
+    default: *keys_per_tile = FwdCfg<256>::BC; *waves = fwd_waves<256, kMaskPattern>(); break;
   }
+  *rows_per_block = 32 * *waves;
 }
 
 }  // namespace exattn

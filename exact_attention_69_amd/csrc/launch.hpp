@@ -50,7 +50,7 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
-// Workgroup geometry of the bf16 kernels, for the pattern plan.
+// Workgroup geometry of the bf16 kernels in pattern mode, for the pattern plan.
 void fwd_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves);
 void bwd_kv_bf16_geometry(int d, int* keys_per_block, int* rows_per_tile, int* waves);
 void bwd_q_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves);
