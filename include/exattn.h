@@ -247,9 +247,10 @@ typedef struct {
  * and rows whose layout row is set in every block; keys that every row sees,
  * likewise) with their index lists, each kernel's per-workgroup tile lists
  * (all built on the device by every call, in stream order, before the
- * attention kernels), the partial results of the full positions'
- * pass (B*H slots of 2d floats per quarter of n), and the backward's row
- * arrays.  Returns 0 for arguments the calls would reject.
+ * attention kernels), a scratch region (about B*H*n*(4d+8) bytes) that holds,
+ * in turn, the copies of the other side's full positions each pass reads
+ * and the partial results of the full positions' passes, and the backward's
+ * row arrays.  Returns 0 for arguments the calls would reject.
  */
 size_t attn_pattern_workspace_bytes(int dtype, int B, int H, int n, int d);
 
