@@ -508,7 +508,7 @@ int attn_fwd_fp8(int B, int H, int n, int d, const void* Q8, const void* K8, con
                  void* stream) {
   int st = check_problem(EXATTN_BF16, B, H, n, d, scale, -1, H);
   if (st != EXATTN_OK) return st;
-  if (d != 128) return EXATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return EXATTN_EUNSUPPORTED;
   if (rotated != 0 && rotated != 1) return EXATTN_EINVAL;
   const void* ptrs[] = {Q8, K8, V8t, O, LSE};
   for (const void* p : ptrs)

@@ -151,14 +151,24 @@ __global__ __launch_bounds__(256) void quant_scale_kernel(float* __restrict__ sc
 constexpr int kF8NW = 8;    // waves (256 query rows per workgroup)
 constexpr int kF8BC = 128;  // keys per tile
 
-// Direct global -> LDS copy of ROWS rows of 128 bytes (global row stride
-// `stride` bytes) into the XOR-swizzled layout of 16-byte chunks used by
-// the bf16 kernels for 128-byte rows.  Rows at or beyond `valid` re-read
-// row valid-1.
-template <int ROWS, int NT>
+// Chunk swizzle of a tile of RB-byte rows (16-byte chunks): 128-byte rows
+// use the bf16 kernels' layout for 128-byte rows; 64-byte rows XOR the chunk
+// with bits 1-2 of the row, so that eight consecutive rows reading the same
+// logical chunk hit eight different 16-byte bank groups.
+template <int RB>
+__device__ __forceinline__ int swz8(int row, int c) {
+  static_assert(RB == 64 || RB == 128, "rows of 64 or 128 bytes");
+  if constexpr (RB == 128) return swz_chunk<64>(row, c);
+  else return c ^ ((row >> 1) & 3);
+}
+
+// Direct global -> LDS copy of ROWS rows of RB bytes (global row stride
+// `stride` bytes) into the swizzled layout.  Rows at or beyond `valid`
+// re-read row valid-1.
+template <int ROWS, int RB, int NT>
 __device__ __forceinline__ void tile8_issue(const uint8_t* __restrict__ src, long stride, int valid, uint8_t* lds,
                                             int tid) {
-  constexpr int CPR = 8;
+  constexpr int CPR = RB / 16;
   constexpr int IT = ROWS * CPR / NT;
   static_assert((ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
   const int wave = tid >> 6, lane = tid & 63;
@@ -167,16 +177,17 @@ __device__ __forceinline__ void tile8_issue(const uint8_t* __restrict__ src, lon
     const int slot0 = it * NT + wave * 64;
     const int p = slot0 + lane;
     const int row = p / CPR;
-    const int c = swz_chunk<64>(row, p % CPR);
+    const int c = swz8<RB>(row, p % CPR);
     const int srow = row < valid ? row : valid - 1;
     lds_dma16(src + (long)srow * stride + 16 * c, lds + 16 * slot0);
   }
 }
 
-// 32 contiguous bytes [32*j, 32*j + 32) of a 128-byte row of a swizzled tile.
+// 32 contiguous bytes [32*j, 32*j + 32) of an RB-byte row of a swizzled tile.
+template <int RB>
 __device__ __forceinline__ i32x8 lds_frag32(const uint8_t* tile, int row, int j) {
-  const u32x4 a = *(const u32x4*)(tile + row * 128 + 16 * swz_chunk<64>(row, 2 * j));
-  const u32x4 b = *(const u32x4*)(tile + row * 128 + 16 * swz_chunk<64>(row, 2 * j + 1));
+  const u32x4 a = *(const u32x4*)(tile + row * RB + 16 * swz8<RB>(row, 2 * j));
+  const u32x4 b = *(const u32x4*)(tile + row * RB + 16 * swz8<RB>(row, 2 * j + 1));
   i32x8 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
     const float* __restrict__ q_scale, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n128, int n_qblocks, int total_blocks,
     float scale_log2_base) {
-  static_assert(D == 128, "the FP8 forward is built for d = 128");
+  static_assert(D == 64 || D == 128, "the FP8 forward is built for d = 64 and 128");
   constexpr int NW = kF8NW, BC = kF8BC, BR = 32 * NW, NT = NW * 64;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NDS = D / 64;   // 64-wide d steps of S
@@ -220,12 +231,13 @@ __global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
     }
   }
 
-  auto issue_k = [&](int t, uint8_t* buf) { tile8_issue<BC, NT>(K + (size_t)t * BC * D, D, n - t * BC, buf, tid); };
-  auto issue_v = [&](int t, uint8_t* buf) { tile8_issue<D, NT>(Vt + (size_t)t * BC, n128, D, buf, tid); };
+  // K tile: BC rows of D bytes; V^T tile: D rows of BC bytes
+  auto issue_k = [&](int t, uint8_t* buf) { tile8_issue<BC, D, NT>(K + (size_t)t * BC * D, D, n - t * BC, buf, tid); };
+  auto issue_v = [&](int t, uint8_t* buf) { tile8_issue<D, BC, NT>(Vt + (size_t)t * BC, n128, D, buf, tid); };
   auto compute_s_block = [&](const uint8_t* Ks, int kb, f32x16 (&s)[NKB]) {
     s[kb] = f32x16{};
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma_f8(lds_frag32(Ks, kb * 32 + l32, 2 * ds + hi), qreg[ds], s[kb]);
+    for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma_f8(lds_frag32<D>(Ks, kb * 32 + l32, 2 * ds + hi), qreg[ds], s[kb]);
   };
 
   f32x16 o[NDB];
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
 #pragma unroll
     for (int ps = 0; ps < NPS; ++ps)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] = mfma_f8(lds_frag32(Vs, db * 32 + l32, 2 * ps + hi), pb[ps], o[db]);
+      for (int db = 0; db < NDB; ++db) o[db] = mfma_f8(lds_frag32<BC>(Vs, db * 32 + l32, 2 * ps + hi), pb[ps], o[db]);
 
     wait_all_and_barrier();
   }
@@ -360,15 +372,16 @@ hipError_t launch_quant_fp8(const Fp8QuantParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
-  if (p.d != 128) return hipErrorInvalidValue;
+  if (p.d != 64 && p.d != 128) return hipErrorInvalidValue;
   constexpr int BR = 32 * kF8NW;
   const int nqb = (p.n + BR - 1) / BR;
   const long total = (long)nqb * p.B * p.H;
   if (total > 0x7fffffffL) return hipErrorInvalidValue;
   const float scale_log2 = p.scale / (p.rotated ? (float)p.d : 1.0f) * kLog2e;
-  hipLaunchKernelGGL((fwd_fp8_kernel<128>), dim3((unsigned)total), dim3(kF8NW * 64), 0, stream,
-                     (const uint8_t*)p.q8, (const uint8_t*)p.k8, (const uint8_t*)p.v8t, p.q_scale, p.k_scale,
-                     p.v_scale, (__bf16*)p.o, p.lse, p.n, fp8_padded_n(p.n), nqb, (int)total, scale_log2);
+  auto kernel = p.d == 64 ? fwd_fp8_kernel<64> : fwd_fp8_kernel<128>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(kF8NW * 64), 0, stream, (const uint8_t*)p.q8,
+                     (const uint8_t*)p.k8, (const uint8_t*)p.v8t, p.q_scale, p.k_scale, p.v_scale, (__bf16*)p.o,
+                     p.lse, p.n, fp8_padded_n(p.n), nqb, (int)total, scale_log2);
   return hipGetLastError();
 }
 

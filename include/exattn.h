@@ -303,7 +303,7 @@ int attn_bwd_pattern(int dtype, int B, int H, int n, int d,
  * accumulators hold the keys); columns at or beyond n are zero.
  * attn_fp8_bytes returns the byte size of either layout (0 if invalid).
  *
- * attn_fwd_fp8 (d = 128): O = softmax(S) V with
+ * attn_fwd_fp8 (d = 64 or 128): O = softmax(S) V with
  *   S = scale / (rotated ? d : 1) * q_scale * k_scale * Q8 K8^T,
  *   V = v_scale * V8,
  * both products on the FP8 matrix cores with fp32 accumulation; the
@@ -312,8 +312,7 @@ int attn_bwd_pattern(int dtype, int B, int H, int n, int d,
  * (rotated = 0); V without.  O is bf16 [B, H, n, d], LSE fp32 [B, H, n].
  * Errors: EXATTN_EINVAL for null or misaligned pointers (16 bytes; 4 for
  * the scale and sign arrays), a bad layout or rotated flag, or overlapping
- * outputs; EXATTN_EUNSUPPORTED for d = 256 (quantiser) or d != 128
- * (forward).
+ * outputs; EXATTN_EUNSUPPORTED for d other than 64 or 128.
  */
 typedef enum { EXATTN_FP8_ROWS = 0, EXATTN_FP8_V_TRANSPOSED = 1 } exattn_fp8_layout;
 

@@ -235,7 +235,8 @@ def test_fp8_entry_points_reject_bad_arguments(lib):
     q8, k8, v8, qs, ks, vs, o, lse = ptrs(8)
     f = lambda **kw: lib.attn_fwd_fp8(1, 2, n, kw.get("d", d), q8, k8, kw.get("v8", v8), qs, ks, vs, 0.1,
                                       kw.get("rot", 0), kw.get("o", o), lse, None)
-    assert f(d=64) == EUNSUPPORTED
+    assert f(d=256) == EUNSUPPORTED
+    assert f(d=32) == EUNSUPPORTED
     assert f(rot=2) == EINVAL
     assert f(v8=None) == EINVAL
     assert f(o=ctypes.c_void_p(k8.value + 16)) == EINVAL

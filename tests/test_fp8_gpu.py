@@ -112,15 +112,16 @@ def vmax_of(v):
                for idx in np.ndindex(*v.shape[:-2]))
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("n", [1, 100, 300, 1000])
 @pytest.mark.parametrize("rotate", [False, True])
-def test_fp8_forward_matches_oracle(n, rotate):
-    wl = make_case(1, 2, n, 128, "bf16", seed=29 + n)
+def test_fp8_forward_matches_oracle(n, rotate, d):
+    wl = make_case(1, 2, n, d, "bf16", seed=29 + n + d)
     x = draw_inputs(wl, ("q", "k", "v"))
     signs = draw_signs(wl) if rotate else None
     o, lse = run_fp8(wl, x, signs)
     O, L = oracle.attention_forward_fp8(x["q"], x["k"], x["v"], wl.scale, signs)
-    check_fp8(o, lse, O, L, vmax_of(x["v"]), f"n{n}_rot{int(rotate)}")
+    check_fp8(o, lse, O, L, vmax_of(x["v"]), f"d{d}_n{n}_rot{int(rotate)}")
 
 
 FP8_VARIANTS = [w for w in VARIANTS if w.fp8]

@@ -118,6 +118,8 @@ VARIANTS = [
              note="BigBird: 64-token blocks, 3 local, 2 global, 3 random per block row"),
     Workload("fp8_b2h32_n8192_d128_rot", 2, 32, 8192, 128, "bf16", seed=69009, fp8=True, rotate=True,
              note="FP8 forward: E4M3 inputs with the Hadamard rotation of Q and K"),
+    Workload("fp8_b4h16_n2048_d64_rot", 4, 16, 2048, 64, "bf16", seed=69010, fp8=True, rotate=True,
+             note="FP8 forward at d=64 (the 4x16-head, n=2048 shape)"),
 ]
 
 
