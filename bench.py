@@ -240,7 +240,7 @@ def main(argv=None):
     nk = len(kms)
     fwd_ms = kms[0]
     bwd_ms = sum(kms[1:])
-    peak = PEAK_TFLOPS[wl.dtype]
+    peak = PEAK_TFLOPS["fp8" if wl.fp8 else wl.dtype]
     value = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
 
     # Algorithmic FLOPs per launch of each kernel (pairs = visible (i, j)):
@@ -317,18 +317,18 @@ def main(argv=None):
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8" if wl.fp8 else wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "n": wl.n, "d": wl.d, "window": wl.window,
                    "q_mult": wl.q_mult, "scale": wl.scale},
-        "pct_bf16_peak": round(100.0 * value / peak, 2),
+        "pct_fp8_peak" if wl.fp8 else "pct_bf16_peak": round(100.0 * value / peak, 2),
         "detail": {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
                    "kernel_ms": {names[i]: round(kms[i], 4) for i in range(nk)},
                    "kernel_tflops": {names[i]: round(kernel_flops[i] / (kms[i] * 1e-3) / 1e12, 2)
                                      for i in range(nk) if kernel_flops[i]},
-                   "fwd_tflops": round(fwd_tflops, 2), "bwd_tflops": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 2),
+                   "fwd_tflops": round(fwd_tflops, 2), "bwd_tflops": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None,
                    "flops_per_step": fwd_f + bwd_f, "wall_s_timed": round(wall, 3),
                    "fwd_hbm_gbs_algorithmic": round(hbm_bytes(wl)[0] / (fwd_ms * 1e-3) / 1e9, 1),
-                   "bwd_hbm_gbs_algorithmic": round(hbm_bytes(wl)[1] / (bwd_ms * 1e-3) / 1e9, 1)},
+                   "bwd_hbm_gbs_algorithmic": round(hbm_bytes(wl)[1] / (bwd_ms * 1e-3) / 1e9, 1) if bwd_ms else None},
         "roofline": roofline,
     }
     if variants:

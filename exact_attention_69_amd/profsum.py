@@ -33,7 +33,8 @@ def kernel_source_sha256():
 
 KERNEL_RE = re.compile(r"(fwd_bf16_kernel|bwd_kv_bf16_kernel|bwd_q_bf16_kernel|bwd_rowdot_kernel|fwd_f32_kernel|"
                        r"bwd_kv_f32_kernel|bwd_q_f32_kernel|pattern_bitmap_kernel|pattern_list_kernel|"
-                       r"pattern_layout_full_kernel|fwd_full_merge_kernel|full_sum_kernel|fwd_fp8_kernel|quant_\w+?kernel|"
+                       r"pattern_layout_full_kernel|pattern_gather_kernel|fwd_full_merge_kernel|full_sum_kernel|fwd_fp8_kernel|"
+                       r"quant_\w+?kernel|"
                        r"elementwise_kernel|copy\w*)(I\w*?E(?:EvP|Ev$|EEv))?")
 # mask mode (second template argument of the bf16 kernels); the unmasked one is unnamed
 MODE_NAMES = {"1": "window", "2": "pattern", "3": "full"}
@@ -44,6 +45,9 @@ def short(name):
     if not m:
         return name[:60]
     args = re.findall(r"Li(\d+)E", m.group(2) or "")
+    if not args:  # a demangled name: kernel<a, b>(...)
+        t = re.match(r"<([\d, ]+)>", name[m.end(1):])
+        args = [a.strip() for a in t.group(1).split(",")] if t else []
     if not args:
         return m.group(1)
     label = args[0]
