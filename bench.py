@@ -128,13 +128,16 @@ def kernel_names(wl):
     return [f"fwd_{t}_kernel<{d}>", f"bwd_rowdot_kernel<{d}>", f"bwd_kv_{t}_kernel<{d}>", f"bwd_q_{t}_kernel<{d}>"]
 
 
-def time_steps(wl, steps, warmup):
+def time_steps(wl, steps, warmup, graph=False):
     """Run `warmup` untimed and `steps` timed steps of the workload with its
     inputs resident on the GPU; returns (names and average ms of the calls of
     a step, ms per step, wall seconds of the timed region).  Dense workloads
     time the four kernels of a step (forward, rowdot, dK/dV, dQ) one call
     each; sparse-pattern workloads time attn_fwd_pattern and attn_bwd_pattern
-    (each including its plan kernels)."""
+    (each including its plan kernels).  With graph=True the step's calls are
+    captured once in a HIP graph and the graph is replayed instead (the same
+    kernels, without the host's per-call overhead); only the whole steps are
+    timed then."""
     import numpy as np
     import torch
     import exact_attention_69_amd as ea
@@ -150,18 +153,21 @@ def time_steps(wl, steps, warmup):
     lse = torch.empty((wl.B, wl.H, wl.n), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     code = ea.EXATTN_BF16 if wl.dtype == "bf16" else ea.EXATTN_F32
+    # events are recorded on this stream; the calls launch on the current
+    # stream (the same one, except inside a graph capture, where it is the
+    # capture stream)
     stream = torch.cuda.current_stream(dev)
     if wl.fp8:
         from workloads import draw_signs
         sg = torch.from_numpy(draw_signs(wl)).to(dev) if wl.rotate else None
         # inputs quantised once (E4M3 codes resident in HBM); the timed call
         # is the FP8 forward
-        q8, qs = ea.attn_quant_fp8(q, sg, ea.EXATTN_FP8_ROWS, stream=stream)
-        k8, ks = ea.attn_quant_fp8(k, sg, ea.EXATTN_FP8_ROWS, stream=stream)
-        v8, vs = ea.attn_quant_fp8(v, None, ea.EXATTN_FP8_V_TRANSPOSED, stream=stream)
+        q8, qs = ea.attn_quant_fp8(q, sg, ea.EXATTN_FP8_ROWS, stream=None)
+        k8, ks = ea.attn_quant_fp8(k, sg, ea.EXATTN_FP8_ROWS, stream=None)
+        v8, vs = ea.attn_quant_fp8(v, None, ea.EXATTN_FP8_V_TRANSPOSED, stream=None)
         names = [f"fwd_fp8_kernel<{wl.d}>"]
         calls = (lambda: ea.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, q.shape, wl.scale, rotated=wl.rotate, out=o,
-                                         lse=lse, stream=stream),)
+                                         lse=lse, stream=None),)
     elif wl.has_pattern:
         window, glob, layout = draw_pattern(wl)
         pat = ea.AttnPattern(window, torch.from_numpy(glob).to(dev) if len(glob) else None,
@@ -169,9 +175,9 @@ def time_steps(wl, steps, warmup):
         ws = torch.empty(ea.attn_pattern_workspace_bytes(code, wl.B, wl.H, wl.n, wl.d), dtype=torch.uint8,
                          device=dev)
         names = ["attn_fwd_pattern", "attn_bwd_pattern"]
-        calls = (lambda: ea.attn_fwd_pattern(q, k, v, pat, wl.scale, out=o, lse=lse, workspace=ws, stream=stream),
+        calls = (lambda: ea.attn_fwd_pattern(q, k, v, pat, wl.scale, out=o, lse=lse, workspace=ws, stream=None),
                  lambda: ea.attn_bwd_pattern(q, k, v, o, do, lse, pat, wl.scale, workspace=ws, dq=dq, dk=dk, dv=dv,
-                                             stream=stream))
+                                             stream=None))
     else:
         ws = torch.empty(max(ea.attn_bwd_workspace_bytes(code, wl.B, wl.H, wl.n, wl.d), 256), dtype=torch.uint8,
                          device=dev)
@@ -182,14 +188,29 @@ def time_steps(wl, steps, warmup):
         names = kernel_names(wl)
         # The backward runs as its three stage calls (the same three kernels
         # that attn_bwd launches), so that every kernel has its own events.
-        calls = (lambda: attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=stream),
-                 lambda: ea.attn_bwd_rowdot(o, do, lse, workspace=ws, stream=stream),
-                 lambda: attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=stream),
-                 lambda: attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=stream))
+        calls = (lambda: attn_fwd(q, k, v, wl.scale, wl.window, out=o, lse=lse, stream=None),
+                 lambda: ea.attn_bwd_rowdot(o, do, lse, workspace=ws, stream=None),
+                 lambda: attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=None),
+                 lambda: attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=None))
     for _ in range(warmup):
         for c in calls:
             c()
     torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        replay_stream = torch.cuda.current_stream(dev)
+        for e0, e1 in ev:
+            e0.record(replay_stream)
+            g.replay()
+            e1.record(replay_stream)
+        torch.cuda.synchronize()
+        time_steps.last_step_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+        return names, [], statistics.median(time_steps.last_step_ms), 0.0
 
     # Whole steps, bracketed by device syncs, timed with events on the stream
     # the kernels are launched on; one event between consecutive calls.
@@ -303,6 +324,10 @@ def main(argv=None):
                 "tflops": round((cf + cb) / (med * 1e-3) / 1e12, 2), "peak_tflops": cpeak,
                 "pct_peak": round(100.0 * (cf + cb) / (med * 1e-3) / 1e12 / cpeak, 2),
                 "kernel_ms": {cn[i]: round(ck[i], 4) for i in range(len(cn))}}
+            # the same step replayed from a HIP graph (no per-call host overhead)
+            _, _, gms, _ = time_steps(cw, 5 if cw.n >= 32768 else 20, 2, graph=True)
+            configs[cw.name]["step_ms_graph_median"] = round(gms, 4)
+            configs[cw.name]["tflops_graph"] = round((cf + cb) / (gms * 1e-3) / 1e12, 2)
 
     if args.copy_calibration:
         import torch
