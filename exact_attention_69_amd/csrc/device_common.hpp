@@ -183,7 +183,6 @@ struct TileAsync {
 // sequence: a row of zeros (any head dim up to 256) and +infinity.
 __device__ const __bf16 kZeroRow[256] = {};
 __device__ const float kPosInf = __builtin_huge_valf();
-__device__ const float kZeroF = 0.0f;
 
 // As TileAsync, but rows at or beyond `valid` are copied from kZeroRow, so
 // they hold exact zeros in LDS.

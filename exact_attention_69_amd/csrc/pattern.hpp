@@ -75,7 +75,8 @@ constexpr int kFullChunkTiles = 16;  // target tiles per chunk
 
 // Per consumer kernel, written by the plan: [0] number of full positions R,
 // [1] workgroups of positions G = ceil(R / kFullRows), [2] chunks C,
-// [3] tiles per chunk.
+// [3] tiles per chunk.  G * C never exceeds ceil(n / kFullRows), the
+// workgroups per head a full-position launch provides (spare ones return).
 enum FullInfo : int { kFullCount = 0, kFullGroups = 1, kFullChunks = 2, kFullTilesPerChunk = 3, kFullInfoInts = 4 };
 
 struct FullDev {
@@ -91,8 +92,6 @@ __host__ __device__ inline int full_part_rows(int n) {
   const int q = (n + 3) / 4;
   return (q + kFullRows - 1) / kFullRows * kFullRows;
 }
-// Workgroups per head a full-position launch provides (>= G * C).
-__host__ __device__ inline int full_items_per_head(int n) { return (n + kFullRows - 1) / kFullRows; }
 
 // One list to build: workgroups own `R` consecutive positions (queries, or
 // keys when `transposed`), tiles span `T` positions of the other side, `NW`
