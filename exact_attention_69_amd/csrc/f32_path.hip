@@ -7,7 +7,11 @@
 // a backward that recomputes P from the saved log-sum-exp (the unite.ai
 // Flash Attention page, "Entenda a Flash Attention", item 2) -- but on the
 // vector ALU: a row of d values is split over TPR = 8 lanes, each holding
-// d/8 of them, and dot products are finished with xor shuffles.
+// d/8 of them, and dot products are finished with xor shuffles.  The four
+// waves of a workgroup own the same 8 rows (keys) and take every fourth row
+// of each staged tile, so a row's serial chain is a quarter of the other
+// side; their partial results are merged through LDS at the end (the
+// log-sum-exp merge for the forward, sums for the gradients).
 #include <math.h>
 
 #include "bwd_common.hpp"
@@ -17,8 +21,9 @@
 namespace exattn {
 namespace {
 
-constexpr int TPR = 8;          // lanes per row
-constexpr int ROWS = 256 / TPR; // rows per 256-thread block
+constexpr int TPR = 8;                  // lanes per row
+constexpr int SPLIT = 4;                // waves of a block, each over a quarter of every tile
+constexpr int ROWS = 64 / TPR;          // rows (keys) per block, shared by its waves
 // rows per staged LDS tile (two tiles of TK x D floats must fit in 64 KiB)
 template <int D>
 constexpr int tile_rows() { return D == 256 ? 16 : 32; }
@@ -34,7 +39,7 @@ __device__ __forceinline__ float row_sum8(float x) {
 // lanes of a row read 8 consecutive floats (conflict-free LDS access).
 
 // ----------------------------------------------------------------------------
-// Forward: block = 32 query rows; loops over 32-key tiles.
+// Forward: block = 8 query rows; loops over 32-key tiles (16 at d=256).
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
@@ -43,10 +48,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
                                                       int window, int group) {
   constexpr int E = D / TPR;
   constexpr int TK = tile_rows<D>();
-  __shared__ float Ks[TK][D];
-  __shared__ float Vs[TK][D];
+  static_assert(2 * TK * D >= SPLIT * ROWS * D, "the merge reuses the tile buffers");
+  __shared__ float KVs[2][TK][D];           // the K and V tiles; the merge's partial acc
+  __shared__ float stat[SPLIT * ROWS * 2];  // merge: m, l of each wave's share
+  float(&Ks)[TK][D] = KVs[0];
+  float(&Vs)[TK][D] = KVs[1];
   const int head = blockIdx.x / nqb, qb = blockIdx.x - (blockIdx.x / nqb) * nqb;
-  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
+  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = (tid & 63) / TPR, wave = tid >> 6;
   const int row = qb * ROWS + rloc;
   const size_t hoff = (size_t)head * n * D;
   const size_t kv_off = (size_t)(head / group) * n * D;  // shared key/value head
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     q[e] = row < n ? Qg[hoff + (size_t)row * D + TPR * e + sub] : 0.0f;
     acc[e] = 0.0f;
   }
-  float m = -INFINITY, l = 0.0f;
+  float m = -INFINITY, l = 0.0f;  // this wave's share: keys j = wave (mod SPLIT) of every tile
 
   int k_lo = 0, k_hi = n;
   if (window >= 0) band_keys(qb * ROWS, qb * ROWS + ROWS, n, window, &k_lo, &k_hi);
@@ -67,6 +75,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   int key_lo = 0, key_hi = n;
   band_keys(row, row + 1, n, window, &key_lo, &key_hi);
   const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
+  constexpr int TW = TK / SPLIT;  // keys of a tile per wave
   for (int k0 = (k_lo / TK) * TK; k0 < k_hi; k0 += TK) {
     __syncthreads();
     for (int i = tid; i < TK * D; i += 256) {
@@ -76,16 +85,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       Vs[r][c] = ok ? V[(size_t)(k0 + r) * D + c] : 0.0f;
     }
     __syncthreads();
-    float s[TK];
+    float s[TW];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < TK; ++j) {
+    for (int t = 0; t < TW; ++t) {
+      const int j = SPLIT * t + wave;
       float part = 0.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) part = fmaf(q[e], Ks[j][TPR * e + sub], part);
       float sj = row_sum8(part) * scale;
       sj = (unsigned)(k0 + j - key_lo) < key_span ? sj : -INFINITY;
-      s[j] = sj;
+      s[t] = sj;
       mx = fmaxf(mx, sj);
     }
     const float m_new = fmaxf(m, mx);
@@ -95,24 +105,51 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] *= alpha;
 #pragma unroll
-    for (int j = 0; j < TK; ++j) {
-      const float p = expf(s[j] - msub);
+    for (int t = 0; t < TW; ++t) {
+      const int j = SPLIT * t + wave;
+      const float p = expf(s[t] - msub);
       l += p;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = fmaf(p, Vs[j][TPR * e + sub], acc[e]);
     }
     m = m_new;
   }
-  if (row < n) {
-    const float inv = 1.0f / l;
+  // merge of the waves' shares: L = log sum_w exp(L_w) over the partial
+  // (m_w, l_w, acc_w) of each wave, O = sum_w exp(m_w - m) acc_w / l
+  __syncthreads();
+  float* part = &KVs[0][0][0];  // [SPLIT][ROWS][D] partial acc
 #pragma unroll
-    for (int e = 0; e < E; ++e) Og[hoff + (size_t)row * D + TPR * e + sub] = acc[e] * inv;
-    if (sub == 0) LSEg[(size_t)head * n + row] = m + logf(l);
+  for (int e = 0; e < E; ++e) part[(wave * ROWS + rloc) * D + TPR * e + sub] = acc[e];
+  if (sub == 0) {
+    stat[(wave * ROWS + rloc) * 2] = m;
+    stat[(wave * ROWS + rloc) * 2 + 1] = l;
+  }
+  __syncthreads();
+  if (wave == 0 && row < n) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < SPLIT; ++w) mt = fmaxf(mt, stat[(w * ROWS + rloc) * 2]);
+    float f[SPLIT], lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < SPLIT; ++w) {
+      const float mw = stat[(w * ROWS + rloc) * 2];
+      f[w] = mw == -INFINITY ? 0.0f : expf(mw - mt);
+      lt += f[w] * stat[(w * ROWS + rloc) * 2 + 1];
+    }
+    const float inv = 1.0f / lt;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < SPLIT; ++w) o = fmaf(f[w], part[(w * ROWS + rloc) * D + TPR * e + sub], o);
+      Og[hoff + (size_t)row * D + TPR * e + sub] = o * inv;
+    }
+    if (sub == 0) LSEg[(size_t)head * n + row] = mt + logf(lt);
   }
 }
 
 // ----------------------------------------------------------------------------
-// Backward, key side: block = 32 keys; accumulates dK and dV over query tiles.
+// Backward, key side: block = 8 keys; accumulates dK and dV over query tiles.
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
@@ -122,15 +159,17 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
                                                          int nkb, float scale, int window, int group) {
   constexpr int E = D / TPR;
   constexpr int TK = tile_rows<D>();
-  __shared__ float Qs[TK][D];
-  __shared__ float dOs[TK][D];
+  static_assert(2 * TK * D >= SPLIT * ROWS * D, "the merge reuses the tile buffers");
+  __shared__ float QdO[2][TK][D];  // the Q and dO tiles; the merge's partial sums
   __shared__ float Ls[TK], Ds[TK];
+  float(&Qs)[TK][D] = QdO[0];
+  float(&dOs)[TK][D] = QdO[1];
   const int kvh = blockIdx.x / nkb, kb = blockIdx.x - (blockIdx.x / nkb) * nkb;  // key/value head, key block
-  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
+  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = (tid & 63) / TPR, wave = tid >> 6;
   const int key = kb * ROWS + rloc;
   const size_t hoff = (size_t)kvh * n * D;
 
-  float k[E], v[E], dk[E], dv[E];
+  float k[E], v[E], dk[E], dv[E];  // dk, dv: this wave's share (rows r = wave mod SPLIT of every tile)
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     k[e] = key < n ? Kg[hoff + (size_t)key * D + TPR * e + sub] : 0.0f;
@@ -166,7 +205,9 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
         Ds[tid] = ok ? dl[i0 + tid] : 0.0f;
       }
       __syncthreads();
-      for (int r = 0; r < TK; ++r) {
+#pragma unroll 2  // full unrolling hoists every row's LDS loads: 400 registers at d=128
+      for (int t = 0; t < TK / SPLIT; ++t) {
+        const int r = SPLIT * t + wave;
         const int qi = i0 + r;
         float ps = 0.0f, pd = 0.0f;
 #pragma unroll
@@ -187,17 +228,29 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
       }
     }
   }
-  if (key < n) {
+  // sums of the waves' shares, in wave order: dK, then dV
+  float* part = &QdO[0][0][0];  // [SPLIT][ROWS][D]
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      dKg[hoff + (size_t)key * D + TPR * e + sub] = dk[e];
-      dVg[hoff + (size_t)key * D + TPR * e + sub] = dv[e];
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e) part[(wave * ROWS + rloc) * D + TPR * e + sub] = pass == 0 ? dk[e] : dv[e];
+    __syncthreads();
+    if (wave == 0 && key < n) {
+      float* dst = (pass == 0 ? dKg : dVg) + hoff + (size_t)key * D;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float acc = part[rloc * D + TPR * e + sub];
+#pragma unroll
+        for (int w = 1; w < SPLIT; ++w) acc += part[(w * ROWS + rloc) * D + TPR * e + sub];
+        dst[TPR * e + sub] = acc;
+      }
     }
   }
 }
 
 // ----------------------------------------------------------------------------
-// Backward, query side: block = 32 query rows; accumulates dQ over key tiles.
+// Backward, query side: block = 8 query rows; accumulates dQ over key tiles.
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
@@ -207,17 +260,19 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
                                                         int window, int group) {
   constexpr int E = D / TPR;
   constexpr int TK = tile_rows<D>();
-  __shared__ float Ks[TK][D];
-  __shared__ float Vs[TK][D];
+  static_assert(2 * TK * D >= SPLIT * ROWS * D, "the merge reuses the tile buffers");
+  __shared__ float KVs[2][TK][D];  // the K and V tiles; the merge's partial sums
+  float(&Ks)[TK][D] = KVs[0];
+  float(&Vs)[TK][D] = KVs[1];
   const int head = blockIdx.x / nqb, qb = blockIdx.x - (blockIdx.x / nqb) * nqb;
-  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = tid / TPR;
+  const int tid = threadIdx.x, sub = tid & (TPR - 1), rloc = (tid & 63) / TPR, wave = tid >> 6;
   const int row = qb * ROWS + rloc;
   const size_t hoff = (size_t)head * n * D;
   const size_t kv_off = (size_t)(head / group) * n * D;  // shared key/value head
   const float* K = Kg + kv_off;
   const float* V = Vg + kv_off;
 
-  float q[E], g[E], dq[E];
+  float q[E], g[E], dq[E];  // dq: this wave's share (keys j = wave mod SPLIT of every tile)
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     q[e] = row < n ? Qg[hoff + (size_t)row * D + TPR * e + sub] : 0.0f;
@@ -242,7 +297,9 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
       Vs[r][c] = ok ? V[(size_t)(k0 + r) * D + c] : 0.0f;
     }
     __syncthreads();
-    for (int j = 0; j < TK; ++j) {
+#pragma unroll
+    for (int t = 0; t < TK / SPLIT; ++t) {
+      const int j = SPLIT * t + wave;
       const int key = k0 + j;
       float ps = 0.0f, pd = 0.0f;
 #pragma unroll
@@ -259,9 +316,20 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
       for (int e = 0; e < E; ++e) dq[e] = fmaf(ds, Ks[j][TPR * e + sub], dq[e]);
     }
   }
-  if (row < n) {
+  // sum of the waves' shares, in wave order
+  __syncthreads();
+  float* part = &KVs[0][0][0];  // [SPLIT][ROWS][D]
 #pragma unroll
-    for (int e = 0; e < E; ++e) dQg[hoff + (size_t)row * D + TPR * e + sub] = dq[e];
+  for (int e = 0; e < E; ++e) part[(wave * ROWS + rloc) * D + TPR * e + sub] = dq[e];
+  __syncthreads();
+  if (wave == 0 && row < n) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float acc = part[rloc * D + TPR * e + sub];
+#pragma unroll
+      for (int w = 1; w < SPLIT; ++w) acc += part[(w * ROWS + rloc) * D + TPR * e + sub];
+      dQg[hoff + (size_t)row * D + TPR * e + sub] = acc;
+    }
   }
 }
 
