@@ -308,6 +308,20 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
         }
       }
 
+      // Issue each product's two transposed LDS reads kLead products ahead
+      // of it; left to itself the compiler waits on every read right before
+      // its product.  (1.7% faster at d=128, 15% at d=256; at d=64, where
+      // three workgroups share a CU, 3% slower, so not there.)
+      if constexpr (D >= 128) {
+        constexpr int NP = 2 * 2 * NDB, kLead = 2;
+        EXATTN_SCHED(kSchedDSRead, 2 * kLead);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          EXATTN_SCHED(kSchedMFMA, 1);
+          if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
+        }
+      }
+
     }
 
     wait_all_and_barrier();
@@ -565,6 +579,17 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
         const bf16x8 sb = acc_to_operand(dp[st >> 1], st & 1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dq[db] = mfma32(lds_col_frag<D>(Ks, 16 * st, 32 * db, lane), sb, dq[db]);
+      }
+      // As in the key-side pass: transposed reads two products ahead (1.3%
+      // faster at d=128; 12% slower at d=256, so only d=128).
+      if constexpr (D == 128) {
+        constexpr int NP = (BC / 16) * NDB, kLead = 2;
+        EXATTN_SCHED(kSchedDSRead, 2 * kLead);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          EXATTN_SCHED(kSchedMFMA, 1);
+          if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
+        }
       }
 
     }
