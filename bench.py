@@ -75,8 +75,8 @@ def hbm_bytes(wl):
 def measured_traffic(wl, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
     (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size), or None
-    when the summary is for another workload or the kernel sources changed
-    since the counters were taken."""
+    when the summary is for another workload or the kernel's sources (its own
+    file and the shared headers) changed since the counters were taken."""
     import re
     from exact_attention_69_amd.profsum import kernel_source_sha256
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_counters_{wl.name}.md")
@@ -86,10 +86,10 @@ def measured_traffic(wl, kernel):
     if not m:
         return None
     info = json.loads(m.group(1))
-    if info.get("workload") != wl.name or info.get("source_sha256") != kernel_source_sha256():
+    k = info.get("kernels", {}).get(kernel)
+    if info.get("workload") != wl.name or k is None or k.get("source_sha256") != kernel_source_sha256(kernel):
         return None
-    k = info["kernels"].get(kernel)
-    return None if k is None else int(k["hbm_bytes_per_launch"])
+    return int(k["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(wl, seconds):

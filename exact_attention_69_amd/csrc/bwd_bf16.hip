@@ -249,6 +249,18 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
         s = mfma32(lds_row_frag<D>(Qs, l32, ds, hi), kreg[ds], s);
         dp = mfma32(lds_row_frag<D>(dOs, l32, ds, hi), lds_row_frag<D>(vres, wave * 32 + l32, ds, hi), dp);
       }
+      // At d=256 (one wave per SIMD, nothing else to hide the latency) the
+      // row reads of Q, dO and V are issued two steps ahead of their
+      // products: 7% faster there, slower at d=128.
+      if constexpr (D == 256) {
+        constexpr int kLead = 2;
+        EXATTN_SCHED(kSchedDSRead, 3 * kLead);
+#pragma unroll
+        for (int i = 0; i < NDS; ++i) {
+          EXATTN_SCHED(kSchedMFMA, 2);
+          if (i + kLead < NDS) EXATTN_SCHED(kSchedDSRead, 3);
+        }
+      }
 
       // The waves of a SIMD reach this vector phase together; the one in it
       // gets priority, so the other's matrix products fill its gaps (1.3%
@@ -534,6 +546,17 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
         for (int ds = 0; ds < NDS; ++ds) {
           s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
           dp[kb] = mfma32(lds_row_frag<D>(Vs, kb * 32 + l32, ds, hi), greg[ds], dp[kb]);
+        }
+      }
+      // Row reads of K and V two steps ahead of their products (d=256: 4%
+      // faster).
+      if constexpr (D == 256) {
+        constexpr int NS = NKB * NDS, kLead = 2;
+        EXATTN_SCHED(kSchedDSRead, 2 * kLead);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          EXATTN_SCHED(kSchedMFMA, 2);
+          if (i + kLead < NS) EXATTN_SCHED(kSchedDSRead, 2);
         }
       }
 

@@ -23,10 +23,25 @@ import sys
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
-def kernel_source_sha256():
-    """SHA-256 over the kernel sources (names and contents, sorted by name)."""
+def kernel_sources(kernel=None):
+    """Source files a kernel is built from: the file that defines it plus
+    every shared header (all sources when `kernel` is None or not found)."""
+    files = sorted(glob.glob(os.path.join(CSRC, "*")))
+    if kernel is None:
+        return files
+    base = re.match(r"[A-Za-z_0-9]+", kernel).group(0)
+    pat = re.compile(r"__global__[^;{]*?\b" + re.escape(base) + r"\s*\(")
+    home = [f for f in files if pat.search(open(f, encoding="utf-8", errors="replace").read())]
+    if not home:
+        return files
+    return sorted(set(home) | {f for f in files if f.endswith(".hpp")})
+
+
+def kernel_source_sha256(kernel=None):
+    """SHA-256 over the names and contents of kernel_sources(kernel), sorted
+    by name."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for f in kernel_sources(kernel):
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()
@@ -132,8 +147,7 @@ def traffic(directory, workload_name, copy_mib, cmds):
            "| kernel | avg ms (trace) | HBM read MiB (scaled) | HBM write MiB (scaled) | algorithmic read / write "
            "MiB | HBM GB/s | MFMA busy % | clock GHz | LDS bank conflicts | MFMA TFLOP executed |",
            "|---|---|---|---|---|---|---|---|---|---|"]
-    js = {"workload": wl.name, "fetch_scale": round(fs, 6), "write_scale": round(ws, 6),
-          "source_sha256": kernel_source_sha256(), "kernels": {}}
+    js = {"workload": wl.name, "fetch_scale": round(fs, 6), "write_scale": round(ws, 6), "kernels": {}}
     for k, cs in cnt.items():
         if k in copy or "FETCH_SIZE" not in cs or k not in kt:
             continue
@@ -148,10 +162,13 @@ def traffic(directory, workload_name, copy_mib, cmds):
         out.append(f"| {k} | {ms:.3f} | {rd / 2**20:.0f} | {wr / 2**20:.0f} | {algs} | {(rd + wr) / (ms * 1e6):.0f} | "
                    f"{busy:.1f} | {clock:.2f} | {cs.get('SQ_LDS_BANK_CONFLICT', 0.0):.0f} | {mops:.3f} |")
         js["kernels"][k] = {"avg_ms_trace": round(ms, 4), "fetch_kib": round(cs["FETCH_SIZE"], 1),
-                            "write_kib": round(cs["WRITE_SIZE"], 1), "hbm_bytes_per_launch": int(rd + wr)}
+                            "write_kib": round(cs["WRITE_SIZE"], 1), "hbm_bytes_per_launch": int(rd + wr),
+                            "sources": [os.path.basename(f) for f in kernel_sources(k)],
+                            "source_sha256": kernel_source_sha256(k)}
     out += ["", "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE/8 XCDs); clock = "
             "(GRBM_GUI_ACTIVE/8) / trace duration; executed MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", "",
-            "Machine-readable (read by bench.py; valid only while the kernel sources hash to `source_sha256`):",
+            "Machine-readable (read by bench.py; a kernel's entry is valid only while the file that defines it and "
+            "the shared headers, listed in `sources`, still hash to its `source_sha256`):",
             "", "```json", json.dumps(js, indent=1), "```"]
     return "\n".join(out)
 

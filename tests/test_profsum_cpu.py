@@ -1,0 +1,49 @@
+"""Host logic of the profile summaries that bench.py reads: which sources a
+kernel's recorded HBM traffic is keyed to, and that a stale or foreign
+record is refused."""
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from exact_attention_69_amd import profsum  # noqa: E402
+from workloads import workload  # noqa: E402
+
+
+def _names(files):
+    return {os.path.basename(f) for f in files}
+
+
+def test_kernel_sources_are_its_file_and_the_headers():
+    kv = _names(profsum.kernel_sources("bwd_kv_bf16_kernel<128>"))
+    fwd = _names(profsum.kernel_sources("fwd_bf16_kernel<128, window>"))
+    headers = {f for f in _names(profsum.kernel_sources()) if f.endswith(".hpp")}
+    assert "bwd_bf16.hip" in kv and "fwd_bf16.hip" not in kv and headers <= kv
+    assert "fwd_bf16.hip" in fwd and "bwd_bf16.hip" not in fwd and headers <= fwd
+    # an unknown kernel falls back to every source
+    assert _names(profsum.kernel_sources("no_such_kernel")) == _names(profsum.kernel_sources())
+    assert profsum.kernel_source_sha256("bwd_kv_bf16_kernel<128>") != profsum.kernel_source_sha256()
+
+
+def test_measured_traffic_refuses_stale_and_foreign_records(tmp_path, monkeypatch):
+    wl = workload("bf16_b2h32_n8192_d128_q3")
+    kernel = "bwd_kv_bf16_kernel<128>"
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    path = prof / f"hbm_traffic_counters_{wl.name}.md"
+
+    def write(name, sha):
+        js = {"workload": name, "kernels": {kernel: {"hbm_bytes_per_launch": 123, "source_sha256": sha}}}
+        path.write_text("table\n\n```json\n" + json.dumps(js) + "\n```\n")
+
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    write(wl.name, profsum.kernel_source_sha256(kernel))
+    assert bench.measured_traffic(wl, kernel) == 123
+    assert bench.measured_traffic(wl, "bwd_q_bf16_kernel<128>") is None  # not recorded
+    write(wl.name, "0" * 64)  # the kernel changed since the counters were taken
+    assert bench.measured_traffic(wl, kernel) is None
+    write("bf16_b4h16_n2048_d64", profsum.kernel_source_sha256(kernel))  # another workload
+    assert bench.measured_traffic(wl, kernel) is None
