@@ -317,6 +317,16 @@ __global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
     for (int ps = 0; ps < NPS; ++ps)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] = mfma_f8(lds_frag32<BC>(Vs, db * 32 + l32, 2 * ps + hi), pb[ps], o[db]);
+    {  // each product's two LDS reads three products ahead (1.5% faster at
+       // d=128, 6% at d=64; the compiler otherwise waits on them in turn)
+      constexpr int NP = NPS * NDB, kLead = 3;
+      EXATTN_SCHED(kSchedDSRead, 2 * kLead);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        EXATTN_SCHED(kSchedMFMA, 1);
+        if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
+      }
+    }
 
     wait_all_and_barrier();
   }
