@@ -242,8 +242,17 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
       }
     }
     if (act) {
-      // S = Q K^T and dP = dO V^T, lanes indexed by key, registers by query row.
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // S = Q K^T and dP = dO V^T, lanes indexed by key, registers by query
+      // row.  The dP accumulator starts at -D of its rows (the workspace holds
+      // -D; register r of a lane is row 8*(r/4) + 4*hi + r%4 of the tile), so
+      // the product ends as dP - D.
+      f32x16 s = f32x16{}, dp;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 nd4 = *(const f32x4*)(&rowst[buf][1][8 * g + 4 * hi]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dp[4 * g + j] = nd4[j];
+      }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         s = mfma32(lds_row_frag<D>(Qs, l32, ds, hi), kreg[ds], s);
@@ -290,7 +299,6 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
       for (int g = 0; g < 4; ++g) {
         const int rb = 8 * g + 4 * hi;  // rows rb .. rb+3 of the tile
         const f32x4 l4 = *(const f32x4*)(&rowst[buf][0][rb]);
-        const f32x4 d4 = *(const f32x4*)(&rowst[buf][1][rb]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * g + j;
@@ -303,7 +311,7 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
             p = (vis & 1u) ? p : 0.0f;
           }
           s[r] = p;
-          dp[r] = p * (dp[r] - d4[j]);  // dS (unscaled)
+          dp[r] = p * dp[r];  // dS = P (dP - D) (unscaled)
         }
       }
 
@@ -438,7 +446,7 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
   const int my_row = FULL ? (f_slot < f.rows ? full.idx[f_slot] : n) : q0 + wave * 32 + l32;
 
   bf16x8 qreg[NDS], greg[NDS];
-  float lse2, dl;
+  float lse2, ndl;  // LSE*log2(e) and -D of this lane's row
   {
     const bool ok = my_row < n;
     const size_t off = hoff + (size_t)(ok ? my_row : 0) * D + 8 * hi;
@@ -450,7 +458,7 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
       greg[ds] = __builtin_bit_cast(bf16x8, ok ? gs[2 * ds] : u32x4{0, 0, 0, 0});
     }
     lse2 = ok ? LSE2g[(size_t)head * n + my_row] : __builtin_huge_valf();
-    dl = ok ? Dg[(size_t)head * n + my_row] : 0.0f;
+    ndl = ok ? Dg[(size_t)head * n + my_row] : 0.0f;
   }
 
   int k_lo = 0, k_hi = n;
@@ -536,12 +544,17 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
       }
     }
     if (act) {
-      // S^T = K Q^T and dP^T = V dO^T: lanes indexed by query row.
+      // S^T = K Q^T and dP^T = V dO^T: lanes indexed by query row.  The dP
+      // accumulator starts at the row's -D, so the product ends as dP - D
+      // (the 16 registers holding -D stay live through the loop; at d=64 they
+      // would cost a wave per SIMD, so there -D is added afterwards).
+      constexpr bool kNegInit = D != 64;
       f32x16 s[NKB], dp[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = f32x16{};
-        dp[kb] = f32x16{};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[kb][r] = kNegInit ? ndl : 0.0f;
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
           s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
@@ -593,7 +606,7 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
             const uint32_t vis = ((uint32_t)((unsigned)(key - key_lo) < key_span) | lay) & ~(fk >> e);
             p = (vis & 1u) ? p : 0.0f;
           }
-          dp[kb][r] = p * (dp[kb][r] - dl);  // dS^T (unscaled)
+          dp[kb][r] = p * (kNegInit ? dp[kb][r] : dp[kb][r] + ndl);  // dS^T = P^T (dP^T - D) (unscaled)
         }
 
       // dQ^T += K^T dS^T, k along the tile's keys.

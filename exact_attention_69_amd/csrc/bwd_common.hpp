@@ -6,9 +6,11 @@
 namespace exattn {
 
 // D_i = sum_k dO_ik * O_ik in fp32 (the row term of dS = P * (dP - D) that
-// the chain rule of the softmax produces), and LSE_i * log2(e), the base-2
-// form of the log-sum-exp that the gradient kernels subtract from their
-// base-2 scores.  Each thread reduces 8 contiguous elements; the D/8 threads
+// the chain rule of the softmax produces), stored negated: the bf16 gradient
+// kernels start the accumulator of the dP product at -D, so the product
+// delivers dP - D and dS takes one multiply per element.  Also LSE_i *
+// log2(e), the base-2 form of the log-sum-exp that the gradient kernels
+// subtract from their base-2 scores.  Each thread reduces 8 contiguous elements; the D/8 threads
 // of a row combine their partial sums with xor shuffles.  rows = B*H*n.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ O, const T* __restrict__ dO,
@@ -28,7 +30,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ O
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (row < rows && part == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;
     lse2[row] = lse[row] * kLog2e;
   }
 }

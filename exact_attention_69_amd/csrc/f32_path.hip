@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
       if (tid < TK) {
         const bool ok = i0 + tid < n;
         Ls[tid] = ok ? lse[i0 + tid] : 0.0f;
-        Ds[tid] = ok ? dl[i0 + tid] : 0.0f;
+        Ds[tid] = ok ? -dl[i0 + tid] : 0.0f;  // the workspace holds -D
       }
       __syncthreads();
 #pragma unroll 2  // full unrolling hoists every row's LDS loads: 400 registers at d=128
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
     dq[e] = 0.0f;
   }
   const float lse = row < n ? LSEg[(size_t)head * n + row] : 0.0f;
-  const float dl = row < n ? Dg[(size_t)head * n + row] : 0.0f;
+  const float dl = row < n ? -Dg[(size_t)head * n + row] : 0.0f;  // the workspace holds -D
 
   int k_lo = 0, k_hi = n;
   if (window >= 0) band_keys(qb * ROWS, qb * ROWS + ROWS, n, window, &k_lo, &k_hi);

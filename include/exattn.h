@@ -108,9 +108,9 @@ int attn_fwd(int dtype, int B, int H, int n, int d,
 
 /*
  * Bytes of device workspace that attn_bwd needs for this problem: two fp32
- * row arrays of [B, H, n] (D = rowsum(dO * O), and LSE * log2(e), the base-2
- * log-sum-exp the gradient kernels use), each starting on a 256-byte
- * boundary.  Returns 0 for arguments that attn_bwd would reject.
+ * row arrays of [B, H, n] (-D, the negated D = rowsum(dO * O), and
+ * LSE * log2(e), the base-2 log-sum-exp the gradient kernels use), each
+ * starting on a 256-byte boundary.  Returns 0 for arguments that attn_bwd would reject.
  */
 size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d);
 
@@ -144,8 +144,10 @@ int attn_bwd(int dtype, int B, int H, int n, int d,
  * mean for attn_bwd; `workspace` carries D from stage 1 to stages 2 and 3
  * and must not be modified in between.
  *
- * attn_bwd_rowdot: D_i = sum_k dO_ik * O_ik and LSE_i * log2(e) (fp32, into
- * the workspace; LSE is the forward's [B, H, n] output).
+ * attn_bwd_rowdot: -D_i, the negated D_i = sum_k dO_ik * O_ik, and
+ * LSE_i * log2(e) (fp32, into the workspace; LSE is the forward's [B, H, n]
+ * output).  D is stored negated because the gradient kernels start the
+ * accumulator of their dP = dO V^T product at -D, which leaves dP - D.
  */
 int attn_bwd_rowdot(int dtype, int B, int H, int n, int d,
                     const void *O, const void *dO, const float *LSE,
