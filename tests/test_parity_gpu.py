@@ -167,3 +167,32 @@ def test_staged_backward_matches_attn_bwd(dtype, window):
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv), ref):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rowdot_workspace_holds_negated_d_and_base2_lse(dtype):
+    """attn_bwd_rowdot's workspace: -D = -rowsum(dO * O) in the first region
+    and LSE * log2(e) in the second (each region starts on a 256-byte
+    boundary), from the O and dO the call was handed."""
+    import torch
+
+    import exact_attention_69_amd as ea
+    from helpers import to_device
+
+    B, H, n, d = 1, 2, 300, 128
+    wl = make_case(B, H, n, d, dtype, seed=31)
+    print(f"[parity] rowdot workspace {wl.name}", flush=True)
+    t = to_device(draw_inputs(wl), dtype)
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale)
+    ws = ea.attn_bwd_rowdot(o, t["do"], lse)
+    torch.cuda.synchronize()
+    rows = B * H * n
+    region = -(-rows * 4 // 256) * 256 // 4
+    w = ws.view(torch.float32).cpu().numpy().astype(np.float64)
+    o64 = o.float().cpu().numpy().astype(np.float64).reshape(rows, d)
+    do64 = t["do"].float().cpu().numpy().astype(np.float64).reshape(rows, d)
+    neg_d = -np.sum(o64 * do64, axis=1)
+    scale = np.max(np.abs(o64)) * np.max(np.abs(do64)) * d
+    assert np.max(np.abs(w[:rows] - neg_d)) <= 1e-6 * scale
+    lse2 = lse.cpu().numpy().astype(np.float64).reshape(rows) * np.log2(np.e)
+    assert np.max(np.abs(w[region:region + rows] - lse2)) <= 1e-6 * np.max(np.abs(lse2))
