@@ -386,7 +386,7 @@ template <int D>
 struct QCfg;
 template <>
 struct QCfg<64> {
-  static constexpr int NW = 4, BC = 64, WPE = 2;
+  static constexpr int NW = 8, BC = 64, WPE = 2;
 };
 template <>
 struct QCfg<128> {
