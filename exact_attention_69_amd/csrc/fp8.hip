@@ -255,6 +255,9 @@ __global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
   f32x16 s_cur[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) compute_s_block(kbuf[0], kb, s_cur);
+  // The first iteration copies tile 2's K rows over tile 0's: every wave must
+  // have read tile 0's K rows for its scores first.
+  wait_all_and_barrier();
 
   for (int j = 0; j < n_tiles; ++j) {
     if (j + 1 < n_tiles) issue_v(j + 1, vbuf[(j + 1) & 1]);

@@ -8,6 +8,21 @@
 
 namespace exattn {
 
+// Compute units of the current device (queried once per device; 256 on
+// MI355X, which is also the fallback if the query fails).
+inline int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    __atomic_store_n(&cache[dev], c, __ATOMIC_RELAXED);
+  }
+  return c;
+}
+
 // Masking modes of the kernels.
 // kMaskFull: the full positions of a pattern (rows or keys gathered from the
 // plan's list), each workgroup over one chunk of the other side's tiles.

@@ -124,6 +124,20 @@ def test_fp8_forward_matches_oracle(n, rotate, d):
     check_fp8(o, lse, O, L, vmax_of(x["v"]), f"d{d}_n{n}_rot{int(rotate)}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_forward_repeats_bit_exact_over_many_workgroups(d):
+    """Regression test for a copy that overwrote the first K tile while other
+    waves could still be reading it: 128-256 workgroups, 20 repeats."""
+    wl = make_case(2, 8, 2048, d, "bf16", q_mult=3.0, seed=43 + d)
+    print(f"[fp8] repeated forward {wl.name}", flush=True)
+    x = draw_inputs(wl, ("q", "k", "v"))
+    signs = draw_signs(wl)
+    o1, l1 = run_fp8(wl, x, signs)
+    for _ in range(20):
+        o2, l2 = run_fp8(wl, x, signs)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 FP8_VARIANTS = [w for w in VARIANTS if w.fp8]
 
 
