@@ -137,6 +137,27 @@ def test_repeated_forward_is_bit_exact_over_many_workgroups(d, window):
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("window", [-1, 300])
+def test_repeated_backward_is_bit_exact_over_many_workgroups(d, window):
+    """The three backward stages on grids of 128-256 workgroups, repeated:
+    every repeat matches the first bit for bit (no atomics, and every tile
+    buffer is refilled only after a barrier that follows its last read)."""
+    import torch
+    import exact_attention_69_amd as ea
+    from helpers import to_device
+    wl = make_case(2, 8, 2048, d, "bf16", window=window, q_mult=3.0, seed=53 + d)
+    print(f"[parity] repeated backward {wl.name}", flush=True)
+    t = to_device(draw_inputs(wl), "bf16")
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], window=window)
+    g1 = ea.attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, window=window)
+    for _ in range(10):
+        g2 = ea.attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, window=window)
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+
+
 def test_dense_d256_two_wave_kernel_matches_oracle_and_one_wave_kernel():
     """d=256 without a window runs a two-waves-per-SIMD forward when the grid
     holds at least two workgroups per CU (here 512 workgroups), else the
