@@ -231,6 +231,10 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
     const int i0 = t * BQ;
 
     bool act = true;
+    // A wave skips the query tiles its 32 keys' band misses (they add
+    // nothing): 5% faster at d=128 with window 512, 3% at d=64; at d=256 (one
+    // wave per SIMD) the branch costs 4-10%, so there every tile runs.
+    if constexpr (WINDOWED && D != 256) act = i0 <= kw0 + 31 + window && kw0 <= i0 + BQ - 1 + window;
     if constexpr (PATTERN) {
       act = wave_live;
       if (act && !gathered) {
@@ -533,6 +537,9 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
     const int kbase = t * BC;
 
     bool act = true;
+    // As in the key-side pass: a wave skips key tiles its rows' band misses,
+    // except at d=256.
+    if constexpr (WINDOWED && D != 256) act = kbase <= rw0 + 31 + window && rw0 <= kbase + BC - 1 + window;
     if constexpr (PATTERN) {
       act = wave_live;
       if (act && !gathered) {
