@@ -561,7 +561,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     // window of n (every key visible; only the ragged tail tile is masked).
     constexpr int kRows = 32 * FwdCfg<256>::RB * FwdCfg<256>::NW;
     const long blocks = (long)((p.n + kRows - 1) / kRows) * p.B * p.H;
-    if (blocks < 2L * device_cu_count()) {
+    if (blocks < 2L * device_cu_count(stream)) {
       FwdParams q = p;
       q.window = p.n;
       return launch_mode<kMaskWindow>(q, stream);

@@ -99,3 +99,15 @@ def test_fp8_step_in_a_graph():
         return ea.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, t["q"].shape, wl.scale, rotated=True)
 
     _replays(wl, static, lambda: run(static), lambda t: dict(zip(("o", "lse"), run(t))), "fp8")
+
+
+def test_dense_d256_forward_on_a_large_grid_in_a_graph():
+    """The two-waves-per-SIMD d=256 forward (a grid of 512 workgroups)."""
+    import exact_attention_69_amd as ea
+    wl = make_case(2, 16, 2048, 256, "bf16", seed=4)
+    static = to_device(draw_inputs(wl, ("q", "k", "v")), "bf16")
+
+    def run(t):
+        return ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale)
+
+    _replays(wl, static, lambda: run(static), lambda t: dict(zip(("o", "lse"), run(t))), "dense d=256")
