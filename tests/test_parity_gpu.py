@@ -158,16 +158,17 @@ def test_repeated_backward_is_bit_exact_over_many_workgroups(d, window):
             assert torch.equal(a, b)
 
 
-def test_dense_d256_two_wave_kernel_matches_oracle_and_one_wave_kernel():
+@pytest.mark.parametrize("n", [2048, 1990])
+def test_dense_d256_two_wave_kernel_matches_oracle_and_one_wave_kernel(n):
     """d=256 without a window runs a two-waves-per-SIMD forward when the grid
-    holds at least two workgroups per CU (here 512 workgroups), else the
-    one-wave kernel.  The whole problem through both (window = n selects the
-    one-wave kernel with every key visible) agrees to bf16 rounding, and two
-    heads match the oracle."""
+    holds at least two workgroups per CU (here 512 workgroups; n=1990 leaves
+    a ragged last tile), else the one-wave kernel.  The whole problem through
+    both (window = n selects the one-wave kernel with every key visible)
+    agrees to bf16 rounding, and two heads match the oracle."""
     import torch
     import exact_attention_69_amd as ea
     from helpers import BF16_LSE_MAX_REL, BF16_O_MAX_REL, to_device
-    B, H, n, d = 2, 16, 2048, 256
+    B, H, d = 2, 16, 256
     wl = make_case(B, H, n, d, "bf16", q_mult=3.0, seed=47)
     print(f"[parity] two-wave d=256 forward {wl.name}", flush=True)
     x = draw_inputs(wl, ("q", "k", "v"))
