@@ -161,3 +161,48 @@ def test_rotation_leaves_exact_attention_unchanged():
     Od, ld = oracle.attention_forward(q, k, v, s)
     np.testing.assert_allclose(Or, Od, rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(lr, ld, rtol=1e-5, atol=1e-5)
+
+
+def test_rotated_attention_on_representable_inputs_equals_dense_oracle():
+    # The rotated branch, pinned exactly: choose the rotated values first.
+    # With M = diag(signs) H (M M^T = d I), Q = Y M^T / d gives Q M = Y, so
+    # the fast Walsh-Hadamard transform of Q * signs returns Y exactly (every
+    # partial sum is a small multiple of 1/64).  Y holds multiples of 1/4 with
+    # absolute maximum 7/4, so each rotated head quantises exactly (codes =
+    # 256 Y, scale 1/256).  The FP8 forward must then reproduce the dense
+    # attention of the unrotated Q, K: the scores (Q M)(K M)^T are d Q K^T, and
+    # only the division by d (not by sqrt(d), not by 1) undoes that.
+    scipy_linalg = pytest.importorskip("scipy.linalg")
+    n, d = 20, 16
+    signs = RNG.choice([-1.0, 1.0], size=d)
+    M = np.diag(signs) @ scipy_linalg.hadamard(d).astype(np.float64)
+    ys = []
+    for _ in range(2):
+        y = RNG.integers(-7, 8, size=(1, 2, n, d)).astype(np.float64) / 4
+        y[..., 0, 0] = 7 / 4  # amax 7/4 in every head
+        ys.append(y)
+    q, k = ((y @ M.T / d).astype(np.float32) for y in ys)
+    for x, y in zip((q, k), ys):  # the construction is exact in fp32
+        np.testing.assert_array_equal(oracle.fwht_f32(x * signs.astype(np.float32)), y.astype(np.float32))
+    v = RNG.integers(-7, 8, size=(1, 2, n, d)).astype(np.float32) / 8
+    v[..., 0, 0] = 7 / 8
+    for s in (1 / math.sqrt(d), 0.7):
+        O, lse = oracle.attention_forward_fp8(q, k, v, s, signs)
+        Od, ld = oracle.attention_forward(q, k, v, s)
+        np.testing.assert_allclose(O, Od, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, ld, rtol=1e-12, atol=1e-12)
+
+
+def test_rotated_fp8_attention_error_is_bounded():
+    # Random inputs through the rotated branch stay within the quantisation
+    # error of the dense attention of the unrotated inputs.  A score scale off
+    # by sqrt(d) (or not divided by d at all) moves the log-sum-exp by far
+    # more than this bound.
+    n, d = 64, 64
+    signs = RNG.choice([-1.0, 1.0], size=d)
+    q, k, v = (RNG.standard_normal((1, 2, n, d)).astype(np.float32) for _ in range(3))
+    s = 1 / math.sqrt(d)
+    O8, l8 = oracle.attention_forward_fp8(q, k, v, s, signs)
+    Od, ld = oracle.attention_forward(q, k, v, s)
+    assert np.max(np.abs(O8 - Od)) / np.max(np.abs(Od)) < 0.15
+    assert np.max(np.abs(l8 - ld)) < 0.1
