@@ -8,6 +8,8 @@ library is missing or a call fails, an exception is raised.
 """
 
 import ctypes
+import functools
+import inspect
 import math
 import os
 
@@ -170,6 +172,27 @@ def _stream_ptr(t, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_call_stream(fn):
+    """Run an entry point's wrapper with its `stream` argument (when one is
+    given) as the current stream, so that every tensor the wrapper allocates
+    (outputs, workspaces, scratch) belongs to the stream its kernels run on.
+    The caching allocator then hands that memory to another allocation only
+    in that stream's order: a workspace freed when the wrapper returns cannot
+    be reused by work on some other stream while the queued kernels still
+    read it."""
+    pos = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kw):
+        stream = kw.get("stream") if "stream" in kw else (args[pos] if len(args) > pos else None)
+        if stream is None:
+            return fn(*args, **kw)
+        with _torch().cuda.stream(stream):
+            return fn(*args, **kw)
+    return wrapped
+
+
+@_on_call_stream
 def attn_fwd(q, k, v, scale=None, window=-1, out=None, lse=None, stream=None):
     """Forward pass.  Returns (O, LSE): O like q, LSE float32 [B, H, n]."""
     torch = _torch()
@@ -197,6 +220,7 @@ def _check_lse(lse, q):
         raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, n]")
 
 
+@_on_call_stream
 def attn_bwd(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None, dk=None, dv=None, stream=None):
     """Backward pass.  Returns (dQ, dK, dV), each like q."""
     torch = _torch()
@@ -230,6 +254,7 @@ def _workspace(q, code, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+@_on_call_stream
 def attn_bwd_rowdot(o, do, lse, workspace=None, stream=None):
     """Backward stage 1: D = rowsum(dO * O) and LSE*log2(e) into the workspace
     (returned)."""
@@ -247,6 +272,7 @@ def attn_bwd_rowdot(o, do, lse, workspace=None, stream=None):
     return workspace
 
 
+@_on_call_stream
 def attn_bwd_dkdv(q, k, v, do, lse, workspace, scale=None, window=-1, dk=None, dv=None, stream=None):
     """Backward stage 2: dK, dV (needs the workspace from attn_bwd_rowdot)."""
     torch = _torch()
@@ -266,6 +292,7 @@ def attn_bwd_dkdv(q, k, v, do, lse, workspace, scale=None, window=-1, dk=None, d
     return dk, dv
 
 
+@_on_call_stream
 def attn_bwd_dq(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, stream=None):
     """Backward stage 3: dQ (needs the workspace from attn_bwd_rowdot)."""
     torch = _torch()
@@ -288,6 +315,7 @@ def attn_bwd_dq(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, str
 # Grouped-query attention: K, V (and dK, dV) have Hkv heads, Hkv dividing H.
 # ---------------------------------------------------------------------------
 
+@_on_call_stream
 def attn_fwd_gqa(q, k, v, scale=None, window=-1, out=None, lse=None, stream=None):
     """Forward with Hkv = k.shape[1] key/value heads shared by groups of
     H / Hkv consecutive query heads.  Returns (O like q, LSE float32 [B, H, n])."""
@@ -302,6 +330,7 @@ def attn_fwd_gqa(q, k, v, scale=None, window=-1, out=None, lse=None, stream=None
     return out, lse
 
 
+@_on_call_stream
 def attn_bwd_gqa(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None, dk=None, dv=None,
                  stream=None):
     """Backward of attn_fwd_gqa.  Returns (dQ like q, dK like k, dV like v);
@@ -322,6 +351,7 @@ def attn_bwd_gqa(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=
     return dq, dk, dv
 
 
+@_on_call_stream
 def attn_bwd_dkdv_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dk=None, dv=None, stream=None):
     """Backward stage 2 with shared key/value heads: dK, dV like k, v."""
     torch = _torch()
@@ -337,6 +367,7 @@ def attn_bwd_dkdv_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dk=Non
     return dk, dv
 
 
+@_on_call_stream
 def attn_bwd_dq_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, stream=None):
     """Backward stage 3 with shared key/value heads: dQ like q."""
     torch = _torch()
@@ -368,6 +399,7 @@ def _pattern_workspace(q, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+@_on_call_stream
 def attn_fwd_pattern(q, k, v, pattern, scale=None, out=None, lse=None, workspace=None, stream=None):
     """Forward over a sparse pattern (AttnPattern).  Returns (O, LSE)."""
     torch = _torch()
@@ -384,6 +416,7 @@ def attn_fwd_pattern(q, k, v, pattern, scale=None, out=None, lse=None, workspace
     return out, lse
 
 
+@_on_call_stream
 def attn_bwd_pattern(q, k, v, o, do, lse, pattern, scale=None, workspace=None, dq=None, dk=None, dv=None,
                      stream=None):
     """Backward over a sparse pattern (AttnPattern).  Returns (dQ, dK, dV)."""
@@ -411,6 +444,7 @@ def attn_fp8_bytes(B, H, n, d, layout):
     return int(load_library().attn_fp8_bytes(B, H, n, d, layout))
 
 
+@_on_call_stream
 def attn_quant_fp8(x, signs=None, layout=EXATTN_FP8_ROWS, stream=None):
     """Quantise a bf16 [B, H, n, d] tensor to E4M3 codes (uint8 tensor in
     the requested layout) and per-head scales (float32 [B, H])."""
@@ -428,6 +462,7 @@ def attn_quant_fp8(x, signs=None, layout=EXATTN_FP8_ROWS, stream=None):
     return x8, scale
 
 
+@_on_call_stream
 def attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, shape, scale=None, rotated=False, out=None, lse=None,
                  stream=None):
     """FP8 forward on quantised inputs (from attn_quant_fp8; V in the

@@ -271,3 +271,38 @@ def test_rowdot_workspace_holds_negated_d_and_base2_lse(dtype):
     assert np.max(np.abs(w[:rows] - neg_d)) <= 1e-6 * scale
     lse2 = lse.cpu().numpy().astype(np.float64).reshape(rows) * np.log2(np.e)
     assert np.max(np.abs(w[region:region + rows] - lse2)) <= 1e-6 * np.max(np.abs(lse2))
+
+
+def test_explicit_stream_allocations_belong_to_that_stream():
+    """attn_bwd(stream=s) called while another stream is current: the
+    workspace it allocates and frees must not be handed to work on the current
+    stream while s still runs.  A spin kernel holds s back, the call queues
+    behind it, and same-size tensors are then allocated and filled with NaN
+    on the current stream; the gradients must still equal an eager call's bit
+    for bit."""
+    import torch
+    import exact_attention_69_amd as ea
+    from helpers import to_device
+    wl = make_case(1, 2, 300, 128, "bf16", seed=77)
+    print(f"[parity] explicit stream {wl.name}", flush=True)
+    t = to_device(draw_inputs(wl), "bf16")
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"])
+    ref = ea.attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse)
+    torch.cuda.synchronize()
+    ws_bytes = max(ea.attn_bwd_workspace_bytes(ea.EXATTN_BF16, *wl_shape(wl)), 256)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(50_000_000)  # a bounded spin (clock cycles) ahead of the call on s
+    got = ea.attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, stream=s)
+    junk = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda").fill_(0xFF) for _ in range(4)]
+    junk += [torch.empty_like(t["q"]).fill_(float("nan")) for _ in range(3)]
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+    del junk
+
+
+def wl_shape(wl):
+    return wl.B, wl.H, wl.n, wl.d
