@@ -90,6 +90,10 @@ typedef enum {
 
 /*
  * Forward pass: O = softmax(scale * Q K^T) V and LSE, per (b, h).
+ * Defined by: the llmis.ru chapter 3.1 "The cost of attention", section 2
+ * (the attention formula); the running max and sum of its section 5 (and of
+ * the unite.ai page's section "O Algoritmo de Flash Attention") give LSE as
+ * the by-product m + ln(l) that the backward needs.
  *   dtype  : EXATTN_F32 or EXATTN_BF16 (type of Q, K, V and O).
  *   B, H, n, d : batch, heads, sequence length, head dim.
  *   Q, K, V: inputs [B, H, n, d].
@@ -107,7 +111,9 @@ int attn_fwd(int dtype, int B, int H, int n, int d,
              void *stream);
 
 /*
- * Bytes of device workspace that attn_bwd needs for this problem: two fp32
+ * Bytes of device workspace that attn_bwd needs for this problem (the row
+ * term D of the softmax's chain rule, llmis.ru chapter 3.1 section 2
+ * differentiated, and the saved LSE in base 2): two fp32
  * row arrays of [B, H, n] (-D, the negated D = rowsum(dO * O), and
  * LSE * log2(e), the base-2 log-sum-exp the gradient kernels use), each
  * starting on a 256-byte boundary.  Returns 0 for arguments that attn_bwd would reject.
@@ -116,6 +122,11 @@ size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d);
 
 /*
  * Backward pass: gradients of sum(O * dO) with respect to Q, K and V.
+ * Defined by: the chain rule of the llmis.ru chapter 3.1 section 2
+ * definition (the pages print no backward formulas), evaluated the way the
+ * unite.ai page's section "Entenda a Flash Attention", item 2, and the
+ * llmis.ru section 5 describe: P is recomputed from Q, K and LSE instead of
+ * being read back, so no n x n matrix reaches device memory.
  *   Q, K, V : the forward's inputs; O and LSE: the forward's outputs for
  *             exactly these inputs, scale and window (P is recomputed from
  *             them, so a mismatched O or LSE gives wrong gradients).
@@ -155,7 +166,8 @@ int attn_bwd_rowdot(int dtype, int B, int H, int n, int d,
                     void *stream);
 
 /* attn_bwd_dkdv: dK and dV (key-side pass: each workgroup owns a block of
- * keys and sweeps the query tiles of its band). */
+ * keys and sweeps the query tiles of its band).  dV = P^T dO and
+ * dK = scale dS^T Q of the chain rule described at attn_bwd. */
 int attn_bwd_dkdv(int dtype, int B, int H, int n, int d,
                   const void *Q, const void *K, const void *V,
                   const void *dO, const float *LSE,
@@ -165,7 +177,8 @@ int attn_bwd_dkdv(int dtype, int B, int H, int n, int d,
                   void *stream);
 
 /* attn_bwd_dq: dQ (query-side pass: each workgroup owns a block of query
- * rows and sweeps the key tiles of its band, recomputing P and dP). */
+ * rows and sweeps the key tiles of its band, recomputing P and dP).
+ * dQ = scale dS K of the chain rule described at attn_bwd. */
 int attn_bwd_dq(int dtype, int B, int H, int n, int d,
                 const void *Q, const void *K, const void *V,
                 const void *dO, const float *LSE,
@@ -175,7 +188,9 @@ int attn_bwd_dq(int dtype, int B, int H, int n, int d,
                 void *stream);
 
 /*
- * Grouped-query variants: as attn_fwd, attn_bwd, attn_bwd_dkdv and
+ * Grouped-query variants (the grouped-query and multi-query attention the
+ * unite.ai page lists under "FlashAttention-2", item 3, without formulas;
+ * read as below): as attn_fwd, attn_bwd, attn_bwd_dkdv and
  * attn_bwd_dq, with Hkv key/value heads (1 <= Hkv <= H, H % Hkv == 0);
  * K, V, dK and dV are [B, Hkv, n, d], everything else keeps its [B, H, ...]
  * shape.  The workspace is the same as for H heads
@@ -244,7 +259,8 @@ typedef struct {
 } exattn_pattern;
 
 /*
- * Workspace for attn_fwd_pattern and attn_bwd_pattern: the global-token
+ * Workspace for attn_fwd_pattern and attn_bwd_pattern (patterns of the
+ * llmis.ru chapter 3.1 section 3, see above): the global-token
  * bitmap, the full positions (query rows that see every key: global tokens
  * and rows whose layout row is set in every block; keys that every row sees,
  * likewise) with their index lists, each kernel's per-workgroup tile lists
@@ -257,7 +273,10 @@ typedef struct {
 size_t attn_pattern_workspace_bytes(int dtype, int B, int H, int n, int d);
 
 /*
- * Forward and backward over a sparse pattern; arguments as for attn_fwd and
+ * Forward and backward over a sparse pattern (llmis.ru chapter 3.1 section
+ * 3; their block-sparse I/O is the subject of Theorem 4.5 in the
+ * gist.science summary of arXiv 2410.09397, section "Contribuicoes
+ * Principais e Resultados", item 2); arguments as for attn_fwd and
  * attn_bwd (multi-head layout [B, H, n, d]), with the pattern in place of
  * the window.  Only EXATTN_BF16 is supported (EXATTN_EUNSUPPORTED for f32).
  * The workgroups visit only the tiles that hold a visible pair; tiles the
@@ -332,7 +351,8 @@ int attn_fwd_fp8(int B, int H, int n, int d,
                  void *O, float *LSE,
                  void *stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL); the
+ * codes are this library's own convention (the pages define none). */
 const char *exattn_status_string(int status);
 
 #ifdef __cplusplus
