@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     EXATTN_F32,
     EXATTN_FP8_ROWS,
     EXATTN_FP8_V_TRANSPOSED,
+    EXATTN_NOALLOC_SCRATCH_BYTES,
     AttnPattern,
     ExattnError,
     LIB_PATH,
@@ -18,6 +19,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_dq,
     attn_bwd_dq_gqa,
     attn_bwd_gqa,
+    attn_bwd_noalloc,
     attn_bwd_pattern,
     attn_bwd_rowdot,
     attn_bwd_workspace_bytes,

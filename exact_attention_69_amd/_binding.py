@@ -20,7 +20,11 @@ EXATTN_F32 = 0
 EXATTN_BF16 = 1
 EXATTN_FP8_ROWS = 0
 EXATTN_FP8_V_TRANSPOSED = 1
-STATUS = {0: "EXATTN_OK", -1: "EXATTN_EINVAL", -2: "EXATTN_EUNSUPPORTED", -3: "EXATTN_EWORKSPACE", -4: "EXATTN_EHIP"}
+STATUS = {0: "EXATTN_OK", -1: "EXATTN_EINVAL", -2: "EXATTN_EUNSUPPORTED", -3: "EXATTN_EWORKSPACE", -4: "EXATTN_EHIP",
+          -5: "EXATTN_ESCRATCH"}
+# Size of attn_bwd_noalloc's fixed per-GPU scratch buffer (the header's
+# EXATTN_NOALLOC_SCRATCH_BYTES).
+EXATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -80,6 +84,8 @@ def load_library(path=None):
     lib.attn_bwd_workspace_bytes.restype = cs
     lib.attn_bwd.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, vp, cs, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_bwd_noalloc.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, vp]
+    lib.attn_bwd_noalloc.restype = ci
     lib.attn_bwd_rowdot.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, cs, vp]
     lib.attn_bwd_rowdot.restype = ci
     lib.attn_bwd_dkdv.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, cf, ci, vp, vp, vp, cs, vp]
@@ -242,6 +248,25 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None
                                      workspace.numel() * workspace.element_size(), _stream_ptr(q, stream))
     if st != 0:
         raise ExattnError("attn_bwd", st, exattn_status_string(st))
+    return dq, dk, dv
+
+
+@_on_call_stream
+def attn_bwd_noalloc(q, k, v, o, do, lse, scale=None, window=-1, dq=None, dk=None, dv=None, stream=None):
+    """Backward pass through the entry point that allocates nothing (its
+    row arrays live in the library's fixed per-GPU scratch buffer).  Returns
+    (dQ, dK, dV); pass dq, dk, dv to keep this wrapper from allocating them."""
+    torch = _torch()
+    _check_inputs(q, k, v, o, do)
+    _check_lse(lse, q)
+    B, H, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _call("attn_bwd_noalloc", _dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+          (q.device, _stream_ptr(q, stream)))
     return dq, dk, dv
 
 

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 
 namespace {
@@ -51,6 +53,8 @@ const char* exattn_status_string(int status) {
     case EXATTN_EUNSUPPORTED: return "unsupported head dim or dtype (d must be 64, 128 or 256; dtype f32 or bf16)";
     case EXATTN_EWORKSPACE: return "workspace smaller than attn_bwd_workspace_bytes()";
     case EXATTN_EHIP: return "HIP runtime error at kernel launch";
+    case EXATTN_ESCRATCH:
+      return "problem needs more scratch than the fixed buffer of attn_bwd_noalloc (EXATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -228,6 +232,65 @@ int attn_bwd_dq(int dtype, int B, int H, int n, int d, const void* Q, const void
                 size_t workspace_bytes, void* stream) {
   return attn_bwd_dq_gqa(dtype, B, H, H, n, d, Q, K, V, dO, LSE, scale, window, dQ, workspace, workspace_bytes,
                          stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward without allocation: the rowdot stage's -D and LSE*log2(e) rows go
+// to a fixed device array instead of a caller workspace.  Each GPU holds its
+// own copy of the array (from the library's first use on it until the
+// process ends); in host code its name is only a stand-in, so kernels get the
+// device address looked up per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[EXATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device (with it current) and kept.
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return EXATTN_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return EXATTN_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return EXATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_noalloc(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,
+                     const void* O, const void* dO, const float* LSE, float scale, int window, void* dQ, void* dK,
+                     void* dV, void* stream) {
+  // every check attn_bwd makes on these arguments, before any HIP call
+  int st = check_problem(dtype, B, H, n, d, scale, window, H);
+  if (st != EXATTN_OK) return st;
+  const size_t wb = attn_bwd_workspace_bytes(dtype, B, H, n, d);
+  if (wb > (size_t)EXATTN_NOALLOC_SCRATCH_BYTES) return EXATTN_ESCRATCH;
+  const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * n * sizeof(float);
+  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {O, tb}, {dO, tb}, {LSE, lb}};
+  const Span outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}};
+  st = check_bwd(dtype, B, H, H, n, d, scale, window, ins, 6, outs, 3, wb);
+  if (st != EXATTN_OK) return st;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != EXATTN_OK) return st;
+  // the rowdot stage overwrites every row of both regions before the
+  // gradient kernels read them: nothing needs clearing between calls
+  return run_bwd(dtype, bwd_params(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, B, H, n, d, scale, window, 1),
+                 exattn::kStageAll, stream);
 }
 
 }  // extern "C"

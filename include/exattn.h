@@ -68,6 +68,8 @@
  *   EXATTN_EUNSUPPORTED d not in {64, 128, 256}, or an unknown dtype.
  *   EXATTN_EWORKSPACE   workspace smaller than attn_bwd_workspace_bytes().
  *   EXATTN_EHIP         the HIP runtime reported an error at launch.
+ *   EXATTN_ESCRATCH     (attn_bwd_noalloc only) the problem needs more than
+ *                       its fixed scratch buffer.
  */
 #ifndef EXATTN_H
 #define EXATTN_H
@@ -85,7 +87,8 @@ typedef enum {
   EXATTN_EINVAL = -1,
   EXATTN_EUNSUPPORTED = -2,
   EXATTN_EWORKSPACE = -3,
-  EXATTN_EHIP = -4
+  EXATTN_EHIP = -4,
+  EXATTN_ESCRATCH = -5
 } exattn_status;
 
 /*
@@ -186,6 +189,30 @@ int attn_bwd_dq(int dtype, int B, int H, int n, int d,
                 void *dQ,
                 const void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/*
+ * attn_bwd_noalloc: attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, meaning, kernels and results (bit for bit) as
+ * attn_bwd, minus the workspace: the rowdot stage's two fp32 row arrays go
+ * to a fixed device buffer of EXATTN_NOALLOC_SCRATCH_BYTES (16 MiB) that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * makes no hipMalloc/hipFree and no allocating library call.  Problems whose
+ * attn_bwd_workspace_bytes() exceeds the buffer (B*H*n > 2^21 rows) return
+ * EXATTN_ESCRATCH with nothing launched.  All calls on one GPU share its
+ * buffer: two calls that may overlap on one GPU (different streams, or
+ * different threads without ordering) race and must be ordered by the caller.
+ * The buffer keeps the last call's contents; every row a call reads is
+ * written by that call first, so nothing needs clearing.
+ */
+#define EXATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int attn_bwd_noalloc(int dtype, int B, int H, int n, int d,
+                     const void *Q, const void *K, const void *V,
+                     const void *O, const void *dO, const float *LSE,
+                     float scale, int window,
+                     void *dQ, void *dK, void *dV,
+                     void *stream);
 
 /*
  * Grouped-query variants (the grouped-query and multi-query attention the

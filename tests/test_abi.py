@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dkdv_gqa", "attn_bwd_dq",
-                                    "attn_bwd_dq_gqa", "attn_bwd_gqa", "attn_bwd_pattern", "attn_bwd_rowdot",
+                                    "attn_bwd_dq_gqa", "attn_bwd_gqa", "attn_bwd_noalloc", "attn_bwd_pattern", "attn_bwd_rowdot",
                                     "attn_bwd_workspace_bytes", "attn_fp8_bytes", "attn_fwd", "attn_fwd_fp8",
                                     "attn_fwd_gqa", "attn_fwd_pattern", "attn_pattern_workspace_bytes",
                                     "attn_quant_fp8", "exattn_status_string"]
@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, 17):
+    for st in (0, -1, -2, -3, -4, -5, 17):
         s = lib.exattn_status_string(st)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -248,3 +248,29 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         ea.attn_fwd(x, x, x)
+
+
+def test_noalloc_backward_rejects_before_any_hip_call(lib):
+    """attn_bwd_noalloc validates like attn_bwd and refuses problems whose
+    row arrays exceed its fixed scratch buffer (the header's
+    EXATTN_NOALLOC_SCRATCH_BYTES, mirrored by the binding)."""
+    import exact_attention_69_amd as ea
+    text = open(os.path.join(ROOT, "include", "exattn.h")).read()
+    m = re.search(r"#define EXATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ea.EXATTN_NOALLOC_SCRATCH_BYTES
+    ESCRATCH = -5
+    q, k, v, o, do, lse, dq, dk, dv = ptrs(9)
+    call = lambda B=1, H=1, n=128, d=64, dq=dq, scale=0.1, window=-1: lib.attn_bwd_noalloc(
+        1, B, H, n, d, q, k, v, o, do, lse, scale, window, dq, dk, dv, None)
+    # the largest problem that fits: two fp32 row arrays of 2^21 rows
+    rows = ea.EXATTN_NOALLOC_SCRATCH_BYTES // 8
+    assert lib.attn_bwd_workspace_bytes(1, 1, 64, rows // 64, 64) == ea.EXATTN_NOALLOC_SCRATCH_BYTES
+    assert call(H=64, n=rows // 64 + 1) == ESCRATCH
+    assert call(B=2, H=64, n=rows // 64) == ESCRATCH
+    assert call(n=0) == EINVAL
+    assert call(d=80) == EUNSUPPORTED
+    assert call(scale=float("nan")) == EINVAL
+    assert call(window=-2) == EINVAL
+    assert call(dq=None) == EINVAL
+    assert call(dq=do) == EINVAL  # dQ aliases dO
+    assert call(dq=ctypes.c_void_p(q.value + 8)) == EINVAL  # misaligned
