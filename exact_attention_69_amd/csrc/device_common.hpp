@@ -31,6 +31,24 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// A copy of a lane-dependent value that the compiler must treat as new on
+// every evaluation (an empty asm that claims to modify it).  LDS addresses
+// derived from it inside a loop are then recomputed where they are used
+// rather than hoisted and kept live across the loop: a VALU op per address
+// instead of a register per address.
+__device__ __forceinline__ int opaque_lane_value(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// The lane index (0-63), computed afresh (v_mbcnt) at every use, so that no
+// register holds it across a loop.
+__device__ __forceinline__ int fresh_lane_id() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -144,6 +162,17 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds_wave
                : "memory", "m0");
 }
 
+// As lds_dma16, with a wave-uniform global base address (held in scalar
+// registers) and a per-lane 32-bit byte offset from it: a copy then needs no
+// 64-bit address arithmetic on the vector ALU.
+__device__ __forceinline__ void lds_dma16_sb(const void* gbase, uint32_t voff, const void* lds_wave_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 // 4-byte variant (global_load_lds_dword): lane i's 4 bytes land at
 // `lds_wave_base` + 4*i.
 __device__ __forceinline__ void lds_dma4(const void* gsrc, const void* lds_wave_base) {
@@ -175,6 +204,38 @@ struct TileAsync {
       const int c = swz_chunk<D>(row, p % CPR);
       const int srow = row < valid ? row : valid - 1;
       lds_dma16(src + (size_t)srow * D + 8 * c, lds + 8 * slot0);
+    }
+  }
+};
+
+// TileAsync with the per-thread chunk offsets computed once (off[], a few
+// registers) and a scalar tile base: a full tile costs no vector ALU work per
+// copy; the tile that crosses the end of the sequence recomputes its offsets
+// with the rows at or beyond `valid` clamped to row valid-1 (the caller masks
+// them out of every result).  `wave` must be wave-uniform.
+template <int D, int ROWS, int NT>
+struct TileDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int IT = ROWS * CPR / NT;
+  static_assert((ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
+  // byte offset of the chunk copy `it` of thread `tid` brings, read from row `src_row`
+  static __device__ __forceinline__ uint32_t chunk_off(int it, int tid, int src_row) {
+    const int p = it * NT + tid, row = p / CPR;
+    return (uint32_t)(src_row * D + 8 * swz_chunk<D>(row, p % CPR)) * 2u;
+  }
+  static __device__ __forceinline__ void init(int tid, uint32_t (&off)[IT]) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) off[it] = chunk_off(it, tid, (it * NT + tid) / CPR);
+  }
+  static __device__ __forceinline__ void issue(const __bf16* base, const uint32_t (&off)[IT], __bf16* lds, int wave) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) lds_dma16_sb(base, off[it], lds + 8 * (it * NT + wave * 64));
+  }
+  static __device__ __forceinline__ void issue_tail(const __bf16* base, int valid, __bf16* lds, int tid, int wave) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int row = (it * NT + tid) / CPR;
+      lds_dma16_sb(base, chunk_off(it, tid, row < valid ? row : valid - 1), lds + 8 * (it * NT + wave * 64));
     }
   }
 };

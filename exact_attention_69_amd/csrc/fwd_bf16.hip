@@ -204,6 +204,10 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) 
   }
 
   using Tile = TileAsync<D, BC, NT>;
+  using Dma = TileDma<D, BC, NT>;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dma_off[Dma::IT];  // this thread's chunk offsets in a full K or V tile
+  Dma::init(tid, dma_off);
 
   // S^T for one K tile in LDS: lanes = query rows, registers = keys.  Each K
   // fragment feeds the RB row blocks.
@@ -247,7 +251,11 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) 
       Tile::issue((g ? gath + gath_off : src) + (size_t)r0 * D, (g ? n_full_keys : n) - r0, buf, tid);
     } else {
       const int t = tile_at(i);
-      Tile::issue(src + (size_t)t * BC * D, n - t * BC, buf, tid);
+      const __bf16* base = src + (size_t)t * BC * D;
+      if (t * BC + BC <= n)
+        Dma::issue(base, dma_off, buf, wave_s);
+      else
+        Dma::issue_tail(base, n - t * BC, buf, tid, wave_s);
     }
   };
   auto issue_k = [&](int i, __bf16* buf) { issue_kv(K, pat.gath_a, i, buf); };
