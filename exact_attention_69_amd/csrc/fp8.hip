@@ -87,20 +87,35 @@ __global__ __launch_bounds__(256) void quant_clear_kernel(uint32_t* __restrict__
 }
 
 // amax of every head: |x| as uint bits (monotonic for non-negative floats).
+// A workgroup reduces kAmaxRows rows of one head (its four waves take every
+// fourth row) in registers, then across its waves in LDS, and issues one
+// atomic max: a head's rows meet at one address n / kAmaxRows times instead
+// of once per row.
+constexpr int kAmaxRows = 64;
+
 template <int D>
 __global__ __launch_bounds__(256) void quant_amax_kernel(const __bf16* __restrict__ X, const float* __restrict__ signs,
-                                                        uint32_t* __restrict__ amax_bits, int n, long rows) {
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  float x[D / 64];
-  load_rotated_row<D>(X + row * D, signs, lane, x);
+                                                        uint32_t* __restrict__ amax_bits, int n, int chunks) {
+  __shared__ float wave_max[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long head = blockIdx.x / chunks;
+  const int r0 = (int)(blockIdx.x - head * chunks) * kAmaxRows;
+  const int r1 = min(r0 + kAmaxRows, n);
   float m = 0.0f;
+  for (int r = r0 + wave; r < r1; r += 4) {
+    float x[D / 64];
+    load_rotated_row<D>(X + (head * n + r) * D, signs, lane, x);
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) m = fmaxf(m, fabsf(x[e]));
+    for (int e = 0; e < D / 64; ++e) m = fmaxf(m, fabsf(x[e]));
+  }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  if (lane == 0) atomicMax(&amax_bits[row / n], __float_as_uint(m));
+  if (lane == 0) wave_max[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float w = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    atomicMax(&amax_bits[head], __float_as_uint(w));
+  }
 }
 
 // codes; `transposed`: write the V layout described at the top; rows
@@ -358,7 +373,8 @@ int fp8_padded_n(int n) { return (n + kF8BC - 1) / kF8BC * kF8BC; }
 
 hipError_t launch_quant_fp8(const Fp8QuantParams& p, hipStream_t stream) {
   const long heads = (long)p.B * p.H;
-  const long rows = heads * p.n;
+  const int chunks = (p.n + kAmaxRows - 1) / kAmaxRows;  // amax workgroups per head
+  if (heads * chunks > 0x7fffffffL) return hipErrorInvalidValue;
   const int n128 = fp8_padded_n(p.n);
   uint32_t* amax = (uint32_t*)p.scale;
   hipLaunchKernelGGL(quant_clear_kernel, dim3((unsigned)((heads + 255) / 256)), dim3(256), 0, stream, amax,
@@ -366,14 +382,14 @@ hipError_t launch_quant_fp8(const Fp8QuantParams& p, hipStream_t stream) {
   const long code_rows = heads * (p.transposed ? n128 : p.n);
   switch (p.d) {
     case 64:
-      hipLaunchKernelGGL((quant_amax_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
-                         (const __bf16*)p.x, p.signs, amax, p.n, rows);
+      hipLaunchKernelGGL((quant_amax_kernel<64>), dim3((unsigned)(heads * chunks)), dim3(256), 0, stream,
+                         (const __bf16*)p.x, p.signs, amax, p.n, chunks);
       hipLaunchKernelGGL((quant_codes_kernel<64>), dim3((unsigned)((code_rows + 3) / 4)), dim3(256), 0, stream,
                          (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, heads, p.transposed);
       break;
     case 128:
-      hipLaunchKernelGGL((quant_amax_kernel<128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
-                         (const __bf16*)p.x, p.signs, amax, p.n, rows);
+      hipLaunchKernelGGL((quant_amax_kernel<128>), dim3((unsigned)(heads * chunks)), dim3(256), 0, stream,
+                         (const __bf16*)p.x, p.signs, amax, p.n, chunks);
       hipLaunchKernelGGL((quant_codes_kernel<128>), dim3((unsigned)((code_rows + 3) / 4)), dim3(256), 0, stream,
                          (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, heads, p.transposed);
       break;
