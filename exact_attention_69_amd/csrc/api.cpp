@@ -30,8 +30,11 @@ int check_problem(int dtype, int B, int H, int n, int d, float scale, int window
   if (!isfinite(scale) || !(scale > 0.0f)) return EXATTN_EINVAL;
   if (dtype != EXATTN_F32 && dtype != EXATTN_BF16) return EXATTN_EUNSUPPORTED;
   if (d != 64 && d != 128 && d != 256) return EXATTN_EUNSUPPORTED;
-  long long elems = (long long)B * H * n * d;
-  if (elems >= (1LL << 31)) return EXATTN_EINVAL;
+  // Row indices (b, h, i) -> (b*H + h)*n + i are 32-bit in the kernels;
+  // element offsets (row * d) are 64-bit, so a tensor may exceed 2^31
+  // elements.
+  long long rows = (long long)B * H * n;
+  if (rows >= (1LL << 31)) return EXATTN_EINVAL;
   return EXATTN_OK;
 }
 

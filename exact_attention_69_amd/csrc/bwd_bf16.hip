@@ -183,8 +183,8 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
       const int i0 = g ? i * BQ : tile_at(i) * BQ;
       const int valid = (g ? n_full_rows : n) - i0;
       const int qrow = (qh0 + qg) * n + i0;
-      Tile::issue((g ? pat.gath_a : Qg) + qrow * D, valid, tiles[buf][0], tid);
-      Tile::issue((g ? pat.gath_b : dOg) + qrow * D, valid, tiles[buf][1], tid);
+      Tile::issue((g ? pat.gath_a : Qg) + (size_t)qrow * D, valid, tiles[buf][0], tid);
+      Tile::issue((g ? pat.gath_b : dOg) + (size_t)qrow * D, valid, tiles[buf][1], tid);
       if (wave == 0) {  // lanes 0-31: LSE*log2(e) of the tile's rows, lanes 32-63: D
         const int r = qrow + min(l32, valid - 1);
         const float* ls = g ? pat.gath_s0 : LSE2g;

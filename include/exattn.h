@@ -64,7 +64,7 @@
  *                       window < -1, non-finite or
  *                       non-positive scale, a pointer not 16-byte aligned,
  *                       an output buffer overlapping an input buffer, or a
- *                       problem of 2^31 elements or more per tensor.
+ *                       problem of 2^31 rows (B*H*n) or more.
  *   EXATTN_EUNSUPPORTED d not in {64, 128, 256}, or an unknown dtype.
  *   EXATTN_EWORKSPACE   workspace smaller than attn_bwd_workspace_bytes().
  *   EXATTN_EHIP         the HIP runtime reported an error at launch.

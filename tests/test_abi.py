@@ -88,7 +88,8 @@ def bwd(lib, dtype=1, B=1, H=1, n=128, d=64, scale=0.125, window=-1, p=None, ws_
     (dict(scale=float("inf")), EINVAL), (dict(scale=float("nan")), EINVAL),
     (dict(d=32), EUNSUPPORTED), (dict(d=96), EUNSUPPORTED), (dict(d=512), EUNSUPPORTED),
     (dict(dtype=2), EUNSUPPORTED), (dict(dtype=-1), EUNSUPPORTED),
-    (dict(B=1 << 12, H=1 << 12, n=1 << 10, d=64), EINVAL),  # >= 2^31 elements
+    (dict(B=1 << 12, H=1 << 12, n=1 << 10, d=64), EINVAL),  # >= 2^31 rows
+    (dict(B=1 << 11, H=1 << 10, n=1 << 10, d=64), EINVAL),  # exactly 2^31 rows
 ])
 def test_forward_rejects_bad_arguments(lib, kw, expect):
     assert fwd(lib, **kw) == expect
@@ -274,3 +275,12 @@ def test_noalloc_backward_rejects_before_any_hip_call(lib):
     assert call(dq=None) == EINVAL
     assert call(dq=do) == EINVAL  # dQ aliases dO
     assert call(dq=ctypes.c_void_p(q.value + 8)) == EINVAL  # misaligned
+
+
+def test_tensors_past_2_31_elements_are_accepted(lib):
+    """The size limit is on rows (B*H*n < 2^31), not on elements: offsets
+    row * d are 64-bit in the kernels."""
+    rows = (1 << 31) - 1
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, rows, 256) == 2 * (-(-rows * 4 // 256) * 256)
+    assert lib.attn_bwd_workspace_bytes(1, 1 << 11, 1, 1 << 14, 256) == 2 * (1 << 27)  # 2^33 elements per tensor
+    assert lib.attn_fp8_bytes(1, 1 << 17, 1 << 13, 128, 0) == (1 << 37)
