@@ -14,7 +14,9 @@ import math
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libexattn.so")
+# The library built in the package directory; EXATTN_LIBRARY names another
+# build of it (the host-sanitizer build of exact_attention_69_amd.build).
+LIB_PATH = os.environ.get("EXATTN_LIBRARY") or os.path.join(PKG_DIR, "libexattn.so")
 
 EXATTN_F32 = 0
 EXATTN_BF16 = 1

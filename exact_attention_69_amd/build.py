@@ -76,12 +76,63 @@ def build(jobs=None, verbose=False):
     return LIB
 
 
+# Host sanitizers for the C-ABI code (argument validation, size arithmetic,
+# workspace offsets): each -fsanitize= applies to the host compilation only.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "san", "libexattn_san.so")
+
+
+def asan_runtime():
+    """Path of clang's shared AddressSanitizer runtime (to preload into the
+    Python process that loads the sanitizer build), or None."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(verbose=False):
+    """libexattn_san.so: the C-ABI entry points (api.cpp) compiled with host
+    AddressSanitizer and UndefinedBehaviorSanitizer, linked with the kernels'
+    ordinary objects.  For host-only tests of the validation paths (load it
+    with EXATTN_LIBRARY set and the runtime from asan_runtime() preloaded)."""
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    objs = []
+    for src in sources():
+        if os.path.basename(src) == "api.cpp":
+            obj = os.path.join(os.path.dirname(SAN_LIB), "api.cpp.o")
+            cmd = [hipcc(), "-x", "hip"] + common_flags() + ["-g", "-O1"] + SAN_FLAGS + ["-c", src, "-o", obj]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
+            objs.append(obj)
+        else:
+            obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+            if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(src):
+                obj = _compile(src, verbose)
+            objs.append(obj)
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", SAN_LIB] + objs + SAN_FLAGS[:4] + \
+        ["-shared-libsan"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    return SAN_LIB
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("-j", "--jobs", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="also build the host-sanitizer library of the C-ABI code (_build/san/)")
     args = ap.parse_args(argv)
     print(build(args.jobs, args.verbose))
+    if args.sanitize:
+        print(build_sanitized(args.verbose))
 
 
 if __name__ == "__main__":
