@@ -392,66 +392,85 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
   }
 }
 
-// Scheduling of a phase of NF fragment loads, each feeding two matrix
-// products (the two key blocks of a pair): the loads (RPF LDS reads per
+// Scheduling of a phase of NF fragment loads, each feeding MPF matrix
+// products (one per key block of a pair): the loads (RPF LDS reads per
 // fragment) are issued kLead fragments ahead of their products.
-template <int NF, int RPF, int kLead = 2>
+template <int NF, int RPF, int kLead = 2, int MPF = 2>
 __device__ __forceinline__ void pair_sched_products() {
   EXATTN_SCHED(kSchedDSRead, RPF * kLead);
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    EXATTN_SCHED(kSchedMFMA, 2);
+    EXATTN_SCHED(kSchedMFMA, MPF);
     if (f + kLead < NF) EXATTN_SCHED(kSchedDSRead, RPF);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Key side at d=128 without a pattern: paired waves.
+// Key side without a pattern, d = 128 and 256: paired waves.
 // ---------------------------------------------------------------------------
 // The 8 waves form 4 pairs (wave w and wave w+4, which share a SIMD); a pair
-// owns 64 keys.  The P-wave of a pair keeps their K rows in registers, forms
-// S = Q K^T and P = exp(S - LSE) for a query tile, passes P (bf16) to its
-// partner through LDS and accumulates dV += P^T dO.  The dS-wave accumulates
-// dK += dS^T Q with dS = P (dP - D).  Each LDS fragment of Q or dO feeds the
-// products of 64 keys (two 32x32 blocks).  The two waves of a SIMD are kept
-// in opposite phases: in iteration i the P-wave forms S(i) (matrix cores),
-// then P(i) (vector ALU), then dV; the dS-wave first forms dS(i-1) from the
-// dP(i-1) it carries over in registers and the P(i-1) its partner left in LDS
-// (vector ALU), then dK with it and dP(i) for the next iteration (matrix
-// cores), so each wave's vector work runs beside the other's products.
-// The P-wave keeps the K rows of both key blocks in registers; the dS-wave
-// keeps the V rows of its first key block in registers and those of the
-// second in LDS, which leaves registers for the dP it carries over.  The
-// dS-wave's instructions win the SIMD's issue arbitration: its chain of short
-// phases is the one that stalls on LDS reads.
-// Buffers: three Q/dO tiles (tiles i-1 and i are read while i+1 is in
+// owns 32 * NKB keys (NKB = 2 key blocks of 32 at d = 128, one at d = 256).
+// The P-wave of a pair keeps their K rows in registers, forms S = Q K^T and
+// P = exp(S - LSE) for a query tile, passes P (bf16) to its partner through
+// LDS and accumulates dV += P^T dO.  The dS-wave accumulates dK += dS^T Q
+// with dS = P (dP - D).  At d = 128 each LDS fragment of Q or dO feeds the
+// products of both key blocks.  The two waves of a SIMD are kept in opposite
+// phases: in iteration i the P-wave forms S(i) (matrix cores), then P(i)
+// (vector ALU), then dV; the dS-wave first forms dS(i-1) from the dP(i-1) it
+// carries over in registers and the P(i-1) its partner left in LDS (vector
+// ALU), then dK with it and dP(i) for the next iteration (matrix cores), so
+// each wave's vector work runs beside the other's products.
+// The P-wave keeps the K rows of its keys in registers; the dS-wave keeps the
+// V rows of its first key block in registers and, at d = 128, those of the
+// second in LDS, which leaves registers for the dP it carries over.  At
+// d = 256 this splits the 512 accumulator registers a single wave would need
+// for 32 keys (dK and dV, 2 x 256 columns) over the two waves, so two waves
+// per SIMD fit where one did.  The dS-wave's instructions win the SIMD's
+// issue arbitration: its chain of short phases is the one that stalls on LDS
+// reads.  Buffers: three Q/dO tiles (tiles i-1 and i are read while i+1 is in
 // flight) and two P tiles; one barrier per iteration.  LDS read addresses are
 // per-lane bases (the tile buffer's offset added once per iteration) XOR a
 // constant, plus a constant offset: four base registers instead of one per
 // fragment, because every register is taken.
-namespace pairkv {
-constexpr int D = 128, BQ = 32, NBUF = 3;
-// LDS layout (bytes)
-constexpr int kTileBytes = BQ * D * 2;               // one Q or dO tile
-constexpr int kTiles = 0;                            // [buf][Q, dO]
-constexpr int kVres = kTiles + NBUF * 2 * kTileBytes;  // [pair]: V rows of key block 1
-constexpr int kPbuf = kVres + 4 * kTileBytes;        // [buf][pair][block/half][lane] x 16 bytes
-constexpr int kRowst = kPbuf + 2 * 4 * 4 * 64 * 16;  // [buf][LSE*log2(e) / -D][32] floats
-constexpr int kBytes = kRowst + NBUF * 2 * BQ * 4;
-static_assert(kTiles + NBUF * 2 * kTileBytes <= 65536, "tile reads use 16-bit LDS offsets");
-}  // namespace pairkv
+template <int D>
+struct PairKv {
+  static constexpr int NKB = D == 128 ? 2 : 1;  // 32-key blocks per pair
+  static constexpr int BQ = 32, NBUF = 3, NT = 512;
+  static constexpr int BKV = 4 * 32 * NKB;      // keys per workgroup
+  static constexpr int RS = 2 * D;              // bytes per tile row
+  // LDS layout (bytes)
+  static constexpr int kTileBytes = BQ * RS;                       // one Q or dO tile
+  static constexpr int kTiles = 0;                                 // [buf][Q, dO]
+  static constexpr int kVres = kTiles + NBUF * 2 * kTileBytes;     // [pair]: V rows of key block 1 (d = 128)
+  static constexpr int kVresBytes = NKB == 2 ? 4 * 32 * RS : 0;
+  static constexpr int kPbufPair = 2 * NKB * 64 * 16;              // one pair's P tile
+  static constexpr int kPbuf = kVres + kVresBytes;                 // [buf][pair][block, half][lane] x 16 bytes
+  static constexpr int kRowst = kPbuf + 2 * 4 * kPbufPair;         // [buf][LSE*log2(e) / -D][32] floats
+  static constexpr int kBytes = kRowst + NBUF * 2 * BQ * 4;
+  static_assert(kBytes <= 160 * 1024, "one workgroup per CU");
+};
 
-template <int MODE>
+// The key side runs on the paired kernel at d = 256 without a pattern (all
+// keys, or a window's band) and at d = 128 over all keys.  (At d = 128 the
+// band's per-key row limits do not fit the paired waves' registers: the
+// single-wave kernel is faster there.)
+template <int D, int MODE>
+constexpr bool pair_kv_dispatch() {
+  return (D == 256 && (MODE == kMaskNone || MODE == kMaskWindow)) || (D == 128 && MODE == kMaskNone);
+}
+
+template <int D, int MODE>
 __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int n, int n_kblocks, int total_blocks, float scale,
     float scale_log2, int window, int group) {
-  using namespace pairkv;
+  using C = PairKv<D>;
   constexpr bool WINDOWED = MODE == kMaskWindow;
-  constexpr int NT = 512, BKV = 256;
+  constexpr int NKB = C::NKB, BQ = C::BQ, NBUF = C::NBUF, NT = C::NT, BKV = C::BKV, RS = C::RS;
   constexpr int NDS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) char lds[kBytes];
+  constexpr int kTileBytes = C::kTileBytes, kTiles = C::kTiles, kRowst = C::kRowst;
+  __shared__ __attribute__((aligned(16))) char lds[C::kBytes];
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int kvh = bid / n_kblocks;
@@ -464,10 +483,10 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
   const size_t hoff = (size_t)kvh * n * D;
   const int qh0 = kvh * group;
   const int kb0 = kblk * BKV;
-  const int kp0 = kb0 + pair * 64;  // first key of the pair
-  int my_key[2];
-  my_key[0] = kp0 + l32;
-  my_key[1] = kp0 + 32 + l32;
+  const int kp0 = kb0 + pair * 32 * NKB;  // first key of the pair
+  int my_key[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) my_key[kb] = kp0 + 32 * kb + l32;
 
   int q_lo = 0, q_hi = n;
   if constexpr (WINDOWED) band_keys(kb0, kb0 + BKV, n, window, &q_lo, &q_hi);
@@ -476,50 +495,51 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
   const int steps = n_tiles * group;
 
   // Per-lane LDS byte offsets (the tile and buffer parts are constants).
-  // Row fragment ds of a swizzled [rows][128] tile, row l32 (k along d):
-  //   l32*256 + 16*((2 ds + hi) ^ sw(l32)).
+  // Row fragment ds of a swizzled [rows][D] tile, row l32 (k along d):
+  //   l32*RS + 16*((2 ds + hi) ^ sw(l32)).
   // Column fragment (k along rows) of query rows 16*half.., columns
   // 32*db..: two 8-byte transpose reads at rows 16 half + 4 hi + q + 8 s
   // (q = (lane%16)/4, s = 0, 1); their offsets are
-  //   4096 half + 2048 s + (C_s ^ 64 db),
-  //   C_s = (4 hi + q)*256 + 64 q + 16*((2 (g&1) + (L/2)%2) ^ hi ^ 2 s) + 8 (L%2)
+  //   16 RS half + 8 RS s + (C_s ^ 64 db),
+  //   C_s = (4 hi + q)*RS + 64 q + 16*((2 (g&1) + (L/2)%2) ^ hi ^ 2 s) + 8 (L%2)
   // with g = lane/16, L = lane%16 (the swizzle value of those rows is
   // 4 q + (hi ^ 2 s), so the XOR with the chunk index splits by bit fields).
   // Both are a per-lane base XOR a constant: the row base keeps sw(l32)/2 in
   // bits 5-7, which the XOR with 32 ds turns into the swizzled chunk, and
   // C_s keeps q in bits 6-7.  Only the bases stay live across the loop (an
   // XOR per fragment recomputes each offset where it is used).
-  const int row_base = l32 * 256 + 16 * ((hi ^ swz_chunk<D>(l32, 0)) & 1) + 32 * (swz_chunk<D>(l32, 0) >> 1);
+  const int row_base = l32 * RS + 16 * ((hi ^ swz_chunk<D>(l32, 0)) & 1) + 32 * (swz_chunk<D>(l32, 0) >> 1);
   int col_base[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int g = lane >> 4, L = lane & 15, q = L >> 2;
-    col_base[s] = (4 * hi + q) * 256 + 64 * q + 16 * (((2 * (g & 1)) + ((L >> 1) & 1)) ^ hi ^ (2 * s)) + 8 * (L & 1);
+    col_base[s] = (4 * hi + q) * RS + 64 * q + 16 * (((2 * (g & 1)) + ((L >> 1) & 1)) ^ hi ^ (2 * s)) + 8 * (L & 1);
   }
   auto ld_row = [&](int base, int off) { return *(const bf16x8*)(lds + base + off); };
   auto ld_col = [&](int base, int s0_off, int s1_off) {
     const bf16x4 a = lds_read_tr16((const __bf16*)(lds + base + s0_off));
-    const bf16x4 b = lds_read_tr16((const __bf16*)(lds + base + 2048 + s1_off));
+    const bf16x4 b = lds_read_tr16((const __bf16*)(lds + base + 8 * RS + s1_off));
     return cat8(a, b);
   };
 
   // step s: query head qh0 + s / n_tiles, tile t_lo + s % n_tiles
+  using Dma = TileDma<D, BQ, NT>;
   auto load_tile = [&](int s, int buf) {
     const int qg = s / n_tiles;
     const int i0 = (t_lo + (s - qg * n_tiles)) * BQ;
-    // first row of the tile in [B*H*n]; B*H*n*D < 2^31 is checked at the ABI
+    // first row of the tile in [B*H*n] (< 2^31, checked at the ABI)
     const int qrow = (qh0 + qg) * n + i0;
-    // one 16-byte chunk per thread: TileDma's placement; rows past n are
-    // clamped copies (their LSE is +inf: P = 0)
-    using Dma = TileDma<D, BQ, NT>;
-    static_assert(Dma::IT == 1, "one chunk per thread and tile");
+    // TileDma's placement; rows past n are clamped copies (their LSE is
+    // +inf: P = 0)
     __bf16* qd = (__bf16*)(lds + kTiles + (2 * buf) * kTileBytes);
     __bf16* gd = (__bf16*)(lds + kTiles + (2 * buf + 1) * kTileBytes);
     if (i0 + BQ <= n) {
-      // (the chunk offset is recomputed from a fresh lane index: no register
-      // holds it across the loop)
+      // (the chunk offsets are recomputed from a fresh lane index: no
+      // register holds them across the loop)
       const int t = wave * 64 + fresh_lane_id();
-      const uint32_t off[1] = {Dma::chunk_off(0, t, t >> 4)};
+      uint32_t off[Dma::IT];
+#pragma unroll
+      for (int it = 0; it < Dma::IT; ++it) off[it] = Dma::chunk_off(it, t, (it * NT + t) / (D / 8));
       Dma::issue(Qg + (size_t)qrow * D, off, qd, wave);
       Dma::issue(dOg + (size_t)qrow * D, off, gd, wave);
     } else {
@@ -534,11 +554,11 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
     }
   };
   auto tile_row0 = [&](int s) { return (t_lo + s % n_tiles) * BQ; };
-  // a pair skips the query tiles its 64 keys' band misses
+  // a pair skips the query tiles its keys' band misses
   auto pair_sees = [&](int s) -> bool {
     if constexpr (WINDOWED) {
       const int i0 = tile_row0(s);
-      return i0 <= kp0 + 63 + window && kp0 <= i0 + BQ - 1 + window;
+      return i0 <= kp0 + 32 * NKB - 1 + window && kp0 <= i0 + BQ - 1 + window;
     } else {
       return true;
     }
@@ -547,9 +567,9 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
   // complete, then the workgroup synchronises.
   auto end_iteration = [&]() { wait_all_and_barrier(); };
 
-  f32x16 acc[2][NDB];  // dV (P-wave) or dK (dS-wave): [key block][d block], transposed
+  f32x16 acc[NKB][NDB];  // dV (P-wave) or dK (dS-wave): [key block][d block], transposed
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[kb][db] = f32x16{};
 
@@ -561,15 +581,17 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) r[ds] = __builtin_bit_cast(bf16x8, ok ? p[2 * ds] : u32x4{0, 0, 0, 0});
   };
-  // The dS-wave's V rows of the second key block stay in LDS, swizzled like
-  // the tiles and read as fragments each tile.
-  const int res = kVres + pair * kTileBytes;  // wave-uniform
-  if (!pwave) {
+  // At d = 128 the dS-wave's V rows of the second key block stay in LDS,
+  // swizzled like the tiles and read as fragments each tile.
+  const int res = C::kVres + pair * 32 * RS;  // wave-uniform
+  if constexpr (NKB == 2) {
+    if (!pwave) {
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int slot = it * 64 + lane, row = slot >> 4;
-      const int key = min(kp0 + 32 + row, n - 1);  // rows past n: clamped copies, not stored
-      lds_dma16(Vg + hoff + (size_t)key * D + 8 * swz_chunk<D>(row, slot & 15), lds + res + 16 * (it * 64));
+      for (int it = 0; it < 32 * (D / 8) / 64; ++it) {
+        const int slot = it * 64 + lane, row = slot / (D / 8);
+        const int key = min(kp0 + 32 + row, n - 1);  // rows past n: clamped copies, not stored
+        lds_dma16(Vg + hoff + (size_t)key * D + 8 * swz_chunk<D>(row, slot % (D / 8)), lds + res + 16 * (it * 64));
+      }
     }
   }
   const int res_base = row_base + res;  // (res_base ^ 32 ds) = res + (row_base ^ 32 ds)
@@ -579,30 +601,30 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
   __syncthreads();
 
   if (pwave) {
-    bf16x8 kr[2][NDS];  // K rows of the two key blocks
-    load_rows(Kg, my_key[0], kr[0]);
-    load_rows(Kg, my_key[1], kr[1]);
-    const int pw_off = kPbuf + pair * 4 * 1024 + 16 * lane;  // + buffer and chunk constants
-    const int ls_off = kRowst + 16 * hi;                      // + buffer and row-group constants
-    // query rows that see each of this lane's keys through the band
-    int row_lo[2] = {0, 0};
-    unsigned row_span[2] = {0u, 0u};
-    if constexpr (WINDOWED) {
+    bf16x8 kr[NKB][NDS];  // K rows of the pair's key blocks
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) load_rows(Kg, my_key[kb], kr[kb]);
+    const int pw_off = C::kPbuf + pair * C::kPbufPair + 16 * lane;  // + buffer and chunk constants
+    const int ls_off = kRowst + 16 * hi;                           // + buffer and row-group constants
+    // query rows that see each of this lane's keys through the band
+    int row_lo[NKB];
+    unsigned row_span[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      row_lo[kb] = 0;
+      row_span[kb] = 0u;
+      if constexpr (WINDOWED) {
         int lo, hi_r;
         band_keys(my_key[kb], my_key[kb] + 1, n, window, &lo, &hi_r);
         row_lo[kb] = lo;
         row_span[kb] = (unsigned)max(hi_r - lo, 0);
       }
     }
-    // the critical chain (S, then the exponentials, then dV) goes first
-    // whenever both waves of the SIMD could issue
     for (int i = 0; i < steps; ++i) {
       const int b = i % NBUF, bn = b == NBUF - 1 ? 0 : b + 1;
       if (i + 1 < steps) load_tile(i + 1, bn);
       if (pair_sees(i)) {
-        // tile buffer b: Q rows at qt, dO at qt + kTileBytes (bits 14 and up,
+        // tile buffer b: Q rows at qt, dO at qt + kTileBytes (bits 13 and up,
         // clear of the XOR fields)
         const int qt = kTiles + (2 * b) * kTileBytes;
         const int rq = opaque_lane_value(row_base) + qt;
@@ -610,21 +632,23 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
         const int cg1 = opaque_lane_value(col_base[1]) + qt + kTileBytes;
         const int i0 = tile_row0(i);
         // S = Q K^T, lanes indexed by key, registers by query row; each Q
-        // fragment feeds both key blocks
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+        // fragment feeds every key block
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
           const bf16x8 qf = ld_row(0, rq ^ (32 * ds));
-          s[0] = mfma32(qf, kr[0][ds], s[0]);
-          s[1] = mfma32(qf, kr[1][ds], s[1]);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(qf, kr[kb][ds], s[kb]);
         }
-        pair_sched_products<NDS, 1>();
+        pair_sched_products<NDS, 1, 2, NKB>();
         __builtin_amdgcn_sched_barrier(0);
         bool need_mask = false;
-        if constexpr (WINDOWED) need_mask = max(i0 + BQ - 1 - kp0, kp0 + 63 - i0) > window;
-        bf16x8 pb[2][2];
+        if constexpr (WINDOWED) need_mask = max(i0 + BQ - 1 - kp0, kp0 + 32 * NKB - 1 - i0) > window;
+        bf16x8 pb[NKB][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             // LSE*log2(e) of rows 8g + 4hi .. +3
@@ -641,23 +665,24 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
           pb[kb][0] = acc_to_operand(s[kb], 0);
           pb[kb][1] = acc_to_operand(s[kb], 1);
         }
-        // P to the partner wave: lane-private 64 bytes, laid out so that
-        // consecutive lanes write consecutive 16-byte slots
+        // P to the partner wave: lane-private 16 bytes per block and half,
+        // laid out so that consecutive lanes write consecutive 16-byte slots
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *(u32x4*)(lds + pw_off + (i & 1) * 16384 + c * 1024) = __builtin_bit_cast(u32x4, pb[c >> 1][c & 1]);
+        for (int c = 0; c < 2 * NKB; ++c)
+          *(u32x4*)(lds + pw_off + (i & 1) * (4 * C::kPbufPair) + c * 1024) =
+              __builtin_bit_cast(u32x4, pb[c >> 1][c & 1]);
         __builtin_amdgcn_sched_barrier(0);
         // dV^T += dO^T P, k along the tile's query rows; each transposed dO
-        // fragment feeds both key blocks
+        // fragment feeds every key block
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const bf16x8 a = ld_col(4096 * half, cg0 ^ (64 * db), cg1 ^ (64 * db));
-            acc[0][db] = mfma32(a, pb[0][half], acc[0][db]);
-            acc[1][db] = mfma32(a, pb[1][half], acc[1][db]);
+            const bf16x8 a = ld_col(16 * RS * half, cg0 ^ (64 * db), cg1 ^ (64 * db));
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) acc[kb][db] = mfma32(a, pb[kb][half], acc[kb][db]);
           }
-        pair_sched_products<2 * NDB, 2>();
+        pair_sched_products<2 * NDB, 2, 2, NKB>();
       }
       end_iteration();
     }
@@ -666,9 +691,9 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
   } else {
     bf16x8 v0[NDS];  // V rows of the first key block
     load_rows(Vg, my_key[0], v0);
-    const int pw_off = kPbuf + pair * 4 * 1024 + 16 * lane;
+    const int pw_off = C::kPbuf + pair * C::kPbufPair + 16 * lane;
     const int ls_off = kRowst + BQ * 4 + 16 * hi;  // the -D row of a buffer
-    f32x16 dp[2];  // dP - D of the previous iteration's tile
+    f32x16 dp[NKB];  // dP - D of the previous iteration's tile
     __builtin_amdgcn_s_setprio(1);
     for (int i = 0; i <= steps; ++i) {
       const int b = i % NBUF, bn = b == NBUF - 1 ? 0 : b + 1, bp = b == 0 ? NBUF - 1 : b - 1;
@@ -678,11 +703,11 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
         // dK^T += Q^T dS, k along the tile's query rows
         const int qt = kTiles + (2 * bp) * kTileBytes;
         const int cq0 = opaque_lane_value(col_base[0]) + qt, cq1 = opaque_lane_value(col_base[1]) + qt;
-        bf16x8 sb[2][2];
+        bf16x8 sb[NKB][2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2 * NKB; ++c) {
           const int kb = c >> 1, half = c & 1;
-          const u32x4 pw = *(const u32x4*)(lds + pw_off + ((i - 1) & 1) * 16384 + c * 1024);
+          const u32x4 pw = *(const u32x4*)(lds + pw_off + ((i - 1) & 1) * (4 * C::kPbufPair) + c * 1024);
           u32x4 w;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -697,11 +722,11 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const bf16x8 a = ld_col(4096 * half, cq0 ^ (64 * db), cq1 ^ (64 * db));
-            acc[0][db] = mfma32(a, sb[0][half], acc[0][db]);
-            acc[1][db] = mfma32(a, sb[1][half], acc[1][db]);
+            const bf16x8 a = ld_col(16 * RS * half, cq0 ^ (64 * db), cq1 ^ (64 * db));
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) acc[kb][db] = mfma32(a, sb[kb][half], acc[kb][db]);
           }
-        pair_sched_products<2 * NDB, 2>();
+        pair_sched_products<2 * NDB, 2, 2, NKB>();
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i < steps && pair_sees(i)) {
@@ -720,25 +745,25 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
         {
           const bf16x8 gf = ld_row(0, rg);
           dp[0] = mfma32(gf, v0[0], nd);
-          dp[1] = mfma32(gf, ld_row(0, vbase), nd);
+          if constexpr (NKB == 2) dp[1] = mfma32(gf, ld_row(0, vbase), nd);
         }
 #pragma unroll
         for (int ds = 1; ds < NDS; ++ds) {
           const bf16x8 gf = ld_row(0, rg ^ (32 * ds));
           dp[0] = mfma32(gf, v0[ds], dp[0]);
-          dp[1] = mfma32(gf, ld_row(0, vbase ^ (32 * ds)), dp[1]);
+          if constexpr (NKB == 2) dp[1] = mfma32(gf, ld_row(0, vbase ^ (32 * ds)), dp[1]);
         }
-        pair_sched_products<NDS, 2>();
+        pair_sched_products<NDS, NKB, 2, NKB>();
       }
       end_iteration();
     }
   }
 
-  // dV rows (P-wave) or dK rows, scaled (dS-wave), of this lane's two keys
+  // dV rows (P-wave) or dK rows, scaled (dS-wave), of this lane's keys
   const float f = pwave ? 1.0f : scale;
   __bf16* dst = pwave ? dVg : dKg;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     if (my_key[kb] >= n) continue;
     __bf16* row = dst + hoff + (size_t)my_key[kb] * D;
 #pragma unroll
@@ -1091,9 +1116,9 @@ hipError_t bwd_passes(const BwdParams& p, unsigned stages, hipStream_t stream) {
   const PatternDev pkv = W == kMaskFull ? PatternDev{} : p.pattern_kv;
   const PatternDev pq = W == kMaskFull ? PatternDev{} : p.pattern_q;
   if (stages & kStageKV) {
-    if constexpr (D == 128 && W == kMaskNone) {
-      static_assert(BKV == 256, "the paired kernel owns 256 keys per workgroup");
-      hipLaunchKernelGGL((bwd_kv_pair_kernel<W>), dim3((unsigned)tk), dim3(512), 0, stream, (const __bf16*)p.q,
+    if constexpr (pair_kv_dispatch<D, W>()) {
+      static_assert(BKV == PairKv<D>::BKV, "the paired kernel's key block matches the grid");
+      hipLaunchKernelGGL((bwd_kv_pair_kernel<D, W>), dim3((unsigned)tk), dim3(512), 0, stream, (const __bf16*)p.q,
                          (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2, p.delta,
                          (__bf16*)p.dk, (__bf16*)p.dv, p.n, nkb, (int)tk, p.scale, scale_log2, p.window, p.group);
     } else {
