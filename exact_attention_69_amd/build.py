@@ -1,8 +1,9 @@
 """Build libexattn.so (HIP kernels for gfx950 + the C-ABI entry points).
 
-Usage: ``python -m exact_attention_69_amd.build [-j N] [--verbose]``.
+Usage: ``python -m exact_attention_69_amd.build [-j N] [--verbose] [--no-poison] [--sanitize]``.
 Objects go to ``_build/`` at the repository root; the shared library is
-written next to this file, where the Python binding loads it from.
+written next to this file, where the Python binding loads it from, and so is
+its LDS-poisoning debug twin, libexattn_poison.so.
 """
 
 import argparse
@@ -46,9 +47,9 @@ def sources():
     return out
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", src, "-o", obj]
+def _compile(src, verbose, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + common_flags() + list(extra) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,20 +61,31 @@ def _compile(src, verbose):
     return obj
 
 
-def build(jobs=None, verbose=False):
+def build(jobs=None, verbose=False, build_dir=BUILD, lib=LIB, extra=()):
     """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+# Debug build whose kernels fill their LDS with NaN bytes before first use
+# (EXATTN_POISON_LDS, device_common.hpp): run against the ordinary build, any
+# read of LDS that the kernel did not write first shows up as a difference.
+# It sits next to the ordinary library so that it travels with the package.
+POISON_LIB = os.path.join(PKG_DIR, "libexattn_poison.so")
+
+
+def build_poisoned(jobs=None, verbose=False):
+    return build(jobs, verbose, os.path.join(BUILD, "poison"), POISON_LIB, ["-DEXATTN_POISON_LDS"])
 
 
 # Host sanitizers for the C-ABI code (argument validation, size arithmetic,
@@ -129,8 +141,12 @@ def main(argv=None):
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--sanitize", action="store_true",
                     help="also build the host-sanitizer library of the C-ABI code (_build/san/)")
+    ap.add_argument("--no-poison", action="store_true",
+                    help="skip the LDS-poisoning debug library (libexattn_poison.so)")
     args = ap.parse_args(argv)
     print(build(args.jobs, args.verbose))
+    if not args.no_poison:
+        print(build_poisoned(args.jobs, args.verbose))
     if args.sanitize:
         print(build_sanitized(args.verbose))
 

@@ -88,6 +88,7 @@ __global__ __launch_bounds__((kv_waves<D, MODE>() * 64), KvCfg<D>::WPE) void bwd
   __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BQ * D];  // [buf][Q/dO]
   __shared__ __attribute__((aligned(16))) __bf16 vres[BKV * D];        // this block's V rows
   __shared__ __attribute__((aligned(16))) float rowst[2][2][BQ];       // [buf][LSE*log2(e) / D]
+  poison_lds(tiles, vres, rowst);
 
   int kvh, kblk;  // key/value head (batch-major), key block
   FullItem f{};
@@ -471,6 +472,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
   constexpr int NDS = D / 16, NDB = D / 32;
   constexpr int kTileBytes = C::kTileBytes, kTiles = C::kTiles, kRowst = C::kRowst;
   __shared__ __attribute__((aligned(16))) char lds[C::kBytes];
+  poison_lds(lds);
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int kvh = bid / n_kblocks;
@@ -822,6 +824,7 @@ __global__ __launch_bounds__((q_waves<D, MODE>() * 64), QCfg<D>::WPE) void bwd_q
   constexpr int NDB = D / 32;
 
   __shared__ __attribute__((aligned(16))) __bf16 tiles[2][2][BC * D];  // [buf][K/V]
+  poison_lds(tiles);
 
   int head, qb;
   FullItem f{};

@@ -297,6 +297,28 @@ __device__ __forceinline__ void wait_all_and_barrier() {
   __syncthreads();
 }
 
+// Debug build with EXATTN_POISON_LDS defined: a kernel first fills its LDS
+// arrays with 0xFF bytes (a NaN in bf16, fp32 and fp8 e4m3 alike, -1 in an
+// int), then synchronises, so that a read of LDS that no copy or store of the
+// kernel wrote before it turns into NaN (or a wrong index) in the results.
+// Called at the top of the kernel, where every thread of the workgroup is
+// still present.  Without the macro it does nothing.
+template <typename T>
+__device__ __forceinline__ void poison_one(T& arr) {
+  static_assert(sizeof(T) % 4 == 0, "LDS arrays are filled a word at a time");
+  uint32_t* p = reinterpret_cast<uint32_t*>(&arr);
+  for (int i = (int)threadIdx.x; i < (int)(sizeof(T) / 4); i += (int)blockDim.x) p[i] = 0xffffffffu;
+}
+template <typename... T>
+__device__ __forceinline__ void poison_lds(T&... arrs) {
+#ifdef EXATTN_POISON_LDS
+  (poison_one(arrs), ...);
+  __syncthreads();
+#else
+  ((void)arrs, ...);
+#endif
+}
+
 // MFMA operand with k along d: lane reads 8 consecutive columns
 // [16*ds + 8*(lane/32), +8) of tile row `row`.
 template <int D>

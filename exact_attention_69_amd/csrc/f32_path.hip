@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   static_assert(2 * TK * D >= SPLIT * ROWS * D, "the merge reuses the tile buffers");
   __shared__ float KVs[2][TK][D];           // the K and V tiles; the merge's partial acc
   __shared__ float stat[SPLIT * ROWS * 2];  // merge: m, l of each wave's share
+  poison_lds(KVs, stat);
   float(&Ks)[TK][D] = KVs[0];
   float(&Vs)[TK][D] = KVs[1];
   const int head = blockIdx.x / nqb, qb = blockIdx.x - (blockIdx.x / nqb) * nqb;
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
   static_assert(2 * TK * D >= SPLIT * ROWS * D, "the merge reuses the tile buffers");
   __shared__ float QdO[2][TK][D];  // the Q and dO tiles; the merge's partial sums
   __shared__ float Ls[TK], Ds[TK];
+  poison_lds(QdO, Ls, Ds);
   float(&Qs)[TK][D] = QdO[0];
   float(&dOs)[TK][D] = QdO[1];
   const int kvh = blockIdx.x / nkb, kb = blockIdx.x - (blockIdx.x / nkb) * nkb;  // key/value head, key block
@@ -262,6 +264,7 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
   constexpr int TK = tile_rows<D>();
   static_assert(2 * TK * D >= SPLIT * ROWS * D, "the merge reuses the tile buffers");
   __shared__ float KVs[2][TK][D];  // the K and V tiles; the merge's partial sums
+  poison_lds(KVs);
   float(&Ks)[TK][D] = KVs[0];
   float(&Vs)[TK][D] = KVs[1];
   const int head = blockIdx.x / nqb, qb = blockIdx.x - (blockIdx.x / nqb) * nqb;

@@ -97,6 +97,7 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_amax_kernel(const __bf16* __restrict__ X, const float* __restrict__ signs,
                                                         uint32_t* __restrict__ amax_bits, int n, int chunks) {
   __shared__ float wave_max[4];
+  poison_lds(wave_max);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long head = blockIdx.x / chunks;
   const int r0 = (int)(blockIdx.x - head * chunks) * kAmaxRows;
@@ -224,6 +225,7 @@ __global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
 
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][BC * D];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][D * BC];
+  poison_lds(kbuf, vbuf);
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int head = bid / n_qblocks;

@@ -106,6 +106,7 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) 
 
   __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 vbuf[2][BC * D];
+  poison_lds(kbuf, vbuf);
 
   int head, qb;
   // full rows: this workgroup's chunk and group of rows

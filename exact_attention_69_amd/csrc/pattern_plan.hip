@@ -2,6 +2,7 @@
 // positions, then for every workgroup of a kernel the list of tiles that hold
 // at least one visible (query, key) pair of a position it stores, each
 // classified as fully visible or partial.
+#include "device_common.hpp"
 #include "pattern.hpp"
 
 namespace exattn {
@@ -64,6 +65,7 @@ struct FullSplits {
 // and how each consumer kernel splits them into workgroups and chunks.
 __global__ __launch_bounds__(1024) void pattern_bitmap_kernel(PlanInput in, FullSplits sp) {
   __shared__ int sh[16];
+  poison_lds(sh);
   const int tid = threadIdx.x, nt = blockDim.x;
   const int n = in.n, nwords = bitmap_words(n), W = (n + 31) / 32;
   for (int w = tid; w < nwords; w += nt) in.gbits[w] = 0u;
@@ -143,6 +145,7 @@ __device__ int count_bits(const uint32_t* bits, int a, int b) {
 // order with wave ballots and a prefix over the four waves.
 __global__ __launch_bounds__(256) void pattern_list_kernel(PlanInput in, PlanList pl) {
   __shared__ int wave_count[4];
+  poison_lds(wave_count);
   const int blk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = in.n;
