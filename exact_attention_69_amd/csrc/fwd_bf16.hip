@@ -483,6 +483,257 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward with paired waves (d = 128 and 256, all keys or a window's band).
+// ---------------------------------------------------------------------------
+// The 8 waves of a workgroup form 4 pairs (wave w and wave w+4 share a SIMD);
+// a pair owns 32 query rows.  The S-wave holds the rows' Q in registers,
+// forms the scores of each key tile, keeps the running maximum and sum of
+// every row and hands P (bf16 MFMA operands) and the rows' rescale factors to
+// its partner through LDS; the O-wave holds the output accumulator and adds
+// P V.  The O-wave runs one tile behind: in iteration i the S-wave works on
+// tile i (matrix products, then exponentials) while the O-wave adds tile i-1
+// (matrix products only), so one wave's vector work can run beside the other
+// wave's products.  This is the producer / consumer split and the overlap of
+// softmax with the matrix products that the unite.ai page "Flash Attention:
+// Revolucionando a Eficiencia dos Modelos Transformer" describes in its
+// section "FlashAttention-3", applied to the two waves of a SIMD.  Splitting
+// the registers this way (Q and the scores in one wave, O in the other) also
+// lets d = 256 run two waves per SIMD, where one wave holding Q and O needed
+// all 512 registers.
+template <int D>
+struct PairFwd {
+  static constexpr int BC = D == 256 ? 32 : 64;  // keys per tile
+  static constexpr int NKB = BC / 32;            // 32-key blocks per tile
+  static constexpr int NT = 512, BR = 128;       // threads; query rows per workgroup
+  static constexpr int kTile = BC * D * 2;       // bytes of one K or V tile
+  // LDS layout (bytes)
+  static constexpr int kK = 0;                       // [2] K tiles
+  static constexpr int kV = kK + 2 * kTile;          // [2] V tiles
+  static constexpr int kPPair = NKB * 2 * 64 * 16;   // one pair's P operands
+  static constexpr int kP = kV + 2 * kTile;          // [2][pair]
+  static constexpr int kA = kP + 2 * 4 * kPPair;     // [2][pair][32 rows] rescale factors (fp32)
+  static constexpr int kBytes = kA + 2 * 4 * 32 * 4;
+  static_assert(kBytes <= 160 * 1024, "one workgroup per CU");
+};
+
+// Used at d = 256.  (At d = 128 the S-wave's exponentials outweigh its
+// partner's products and the kernel that keeps 8 row blocks per workgroup is
+// faster.)
+template <int D, int MODE>
+constexpr bool fwd_pair_dispatch() {
+  return D == 256 && (MODE == kMaskNone || MODE == kMaskWindow);
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(512, 2) void fwd_pair_kernel(const __bf16* __restrict__ Qg,
+                                                          const __bf16* __restrict__ Kg,
+                                                          const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
+                                                          float* __restrict__ LSEg, int n, int n_qblocks,
+                                                          int total_blocks, float scale_log2, int window, int group) {
+  using C = PairFwd<D>;
+  constexpr bool WINDOWED = MODE == kMaskWindow;
+  constexpr int BC = C::BC, NKB = C::NKB, NT = C::NT, BR = C::BR;
+  constexpr int NDS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) char lds[C::kBytes];
+  poison_lds(lds);
+
+  const int bid = xcd_remap(blockIdx.x, total_blocks);
+  const int head = bid / n_qblocks;
+  const int qb = bid - head * n_qblocks;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const bool swave = wave < 4;  // S-wave, else O-wave
+
+  // Query heads [g*group, (g+1)*group) share key/value head g.
+  const size_t head_off = (size_t)head * n * D;
+  const size_t kv_off = (size_t)(head / group) * n * D;
+  const __bf16* K = Kg + kv_off;
+  const __bf16* V = Vg + kv_off;
+  const int q0 = qb * BR;
+  const int w0 = q0 + pair * 32;  // first row of the pair
+  const int my_row = w0 + l32;    // this lane's row (both waves of the pair)
+
+  // key tiles of the workgroup's band (all keys without a window)
+  int k_lo = 0, k_hi = n;
+  if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
+  const int t_lo = k_lo / BC;
+  const int n_tiles = (k_hi + BC - 1) / BC - t_lo;
+
+  // Every thread of the workgroup takes part in every copy.  Key rows past n
+  // are clamped copies; their scores are masked (P = 0).
+  using Dma = TileDma<D, BC, NT>;
+  uint32_t dma_off[Dma::IT];
+  Dma::init(tid, dma_off);
+  auto issue = [&](const __bf16* src, int i, int buf_off) {
+    const int t = t_lo + i;
+    const __bf16* base = src + (size_t)t * BC * D;
+    __bf16* dst = (__bf16*)(lds + buf_off);
+    if (t * BC + BC <= n)
+      Dma::issue(base, dma_off, dst, wave);
+    else
+      Dma::issue_tail(base, n - t * BC, dst, tid, wave);
+  };
+  // Copies of iteration i: K of tile i+1 (read by the S-wave in iteration
+  // i+1) and V of tile i (read by the O-wave in iteration i+1), each into the
+  // buffer of its kind read in iteration i-1 (released by that iteration's
+  // barrier).
+  auto issue_iteration = [&](int i) {
+    if (i + 1 < n_tiles) issue(K, i + 1, C::kK + ((i + 1) & 1) * C::kTile);
+    if (i < n_tiles) issue(V, i, C::kV + (i & 1) * C::kTile);
+  };
+  // a pair skips the key tiles its rows' band misses
+  auto pair_sees = [&](int i) -> bool {
+    if constexpr (WINDOWED) {
+      const int c0 = (t_lo + i) * BC;
+      return c0 <= w0 + 31 + window && w0 <= c0 + BC - 1 + window;
+    } else {
+      return true;
+    }
+  };
+  const int p_off = C::kP + pair * C::kPPair + 16 * lane;  // + buffer * 4 * kPPair + operand * 1024
+  const int a_off = C::kA + pair * 128 + 4 * l32;          // + buffer * 512
+
+  // The S-wave's Q^T operands (lane: Q[my_row][16*ds + 8*hi .. +8]) are
+  // loaded before the first wait, which then covers them: the compiler's own
+  // wait for these loads would otherwise sit inside the loop, where it would
+  // also wait for the copies just issued.
+  bf16x8 qreg[NDS];
+  if (swave) {
+    const bool ok = my_row < n;
+    const u32x4* src = (const u32x4*)(Qg + head_off + (size_t)(ok ? my_row : 0) * D + 8 * hi);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qreg[ds] = __builtin_bit_cast(bf16x8, ok ? src[2 * ds] : u32x4{0, 0, 0, 0});
+  }
+  if (n_tiles > 0) issue(K, 0, C::kK);
+  wait_all_and_barrier();
+
+  if (swave) {
+    // keys this lane's row sees: [key_lo, key_lo + key_span)
+    int key_lo = 0, key_hi = n;
+    if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
+    const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
+    float m_run = kNegInf, l_part = 0.0f;  // running max (log2 domain), this lane's share of the sum
+
+    for (int i = 0; i <= n_tiles; ++i) {
+      issue_iteration(i);
+      if (i < n_tiles && pair_sees(i)) {
+        const __bf16* Ks = (const __bf16*)(lds + C::kK + (i & 1) * C::kTile);
+        const int kbase = (t_lo + i) * BC;
+        // S^T = K Q^T: lanes = the pair's rows, registers = keys
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          s[kb] = f32x16{};
+#pragma unroll
+          for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma32(lds_row_frag<D>(Ks, kb * 32 + l32, ds, hi), qreg[ds], s[kb]);
+        }
+        // masks: the key tail and the band
+        bool need_mask = kbase + BC > n;
+        if constexpr (WINDOWED) need_mask = need_mask || max(w0 + 31 - kbase, kbase + BC - 1 - w0) > window;
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbase + kb * 32 + acc_row(r, lane);
+              s[kb][r] = (unsigned)(key - key_lo) < key_span ? s[kb][r] : kNegInf;
+            }
+        }
+        // running max with the lazy rescale: the max used for the
+        // exponentials is raised only when a row's max exceeds it by more
+        // than kRescaleThreshold; alpha (1 otherwise) rescales O and the sum
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        const float mx2 = pair_max(mx) * scale_log2;  // -inf stays -inf
+        const bool grow = mx2 > m_run + kRescaleThreshold || (m_run == kNegInf && mx2 != kNegInf);
+        const float alpha = grow ? fast_exp2(m_run - mx2) : 1.0f;  // m_run = -inf: 0
+        if (grow) m_run = mx2;
+        l_part *= alpha;
+        const float msub = m_run == kNegInf ? 0.0f : m_run;
+        // P = 2^(scale*log2e*s - m), its bf16 operands, and the row sum
+        bf16x8 pb[2 * NKB];
+        float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -msub));
+            lsum[r & 3] += s[kb][r];
+          }
+          pb[2 * kb] = acc_to_operand(s[kb], 0);
+          pb[2 * kb + 1] = acc_to_operand(s[kb], 1);
+        }
+        l_part += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+        // to the O-wave: lane-private 16-byte slots, consecutive lanes in
+        // consecutive slots; the factor once per row
+        const int b = i & 1;
+#pragma unroll
+        for (int c = 0; c < 2 * NKB; ++c)
+          *(u32x4*)(lds + p_off + b * (4 * C::kPPair) + c * 1024) = __builtin_bit_cast(u32x4, pb[c]);
+        if (hi == 0) *(float*)(lds + a_off + b * 512) = alpha;
+      }
+      wait_all_and_barrier();
+    }
+    // 1/l of each row to the O-wave; the log-sum-exp, ln 2 * (m + log2 l)
+    // (a row that saw no key: LSE = -inf)
+    const float l_tot = pair_sum(l_part);
+    if (hi == 0) {
+      *(float*)(lds + a_off) = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      if (my_row < n) LSEg[(size_t)head * n + my_row] = l_tot > 0.0f ? kLn2 * (m_run + fast_log2(l_tot)) : kNegInf;
+    }
+    __syncthreads();
+  } else {
+    // O^T (d x rows) accumulator: lanes = the pair's rows
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    for (int i = 0; i <= n_tiles; ++i) {
+      issue_iteration(i);
+      if (i >= 1 && pair_sees(i - 1)) {
+        const int b = (i - 1) & 1;
+        const float alpha = *(const float*)(lds + a_off + b * 512);
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        bf16x8 pb[2 * NKB];
+#pragma unroll
+        for (int c = 0; c < 2 * NKB; ++c) pb[c] = *(const bf16x8*)(lds + p_off + b * (4 * C::kPPair) + c * 1024);
+        // O^T += V^T P^T: V^T through the transpose read, in the k order of
+        // the P operands
+        const __bf16* Vs = (const __bf16*)(lds + C::kV + b * C::kTile);
+#pragma unroll
+        for (int st = 0; st < BC / 16; ++st)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[db] = mfma32(lds_col_frag<D>(Vs, 16 * st, 32 * db, lane), pb[st], o[db]);
+      }
+      wait_all_and_barrier();
+    }
+    __syncthreads();  // the S-wave's 1/l
+    const float inv = *(const float*)(lds + a_off);
+    if (my_row < n) {
+      __bf16* Orow = Og + head_off + (size_t)my_row * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dd = db * 32 + 8 * g + 4 * hi;
+          u32x2 w;
+          w[0] = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+          w[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+          *(u32x2*)(Orow + dd) = w;
+        }
+    }
+  }
+}
+
 // Merge of the full rows' chunks (when there are several): with each
 // chunk's normalised O_c and log-sum-exp L_c, L = log sum_c exp(L_c) and
 // O = sum_c exp(L_c - L) O_c (the two-block merge of the online softmax,
@@ -525,6 +776,16 @@ __global__ __launch_bounds__(256) void fwd_full_merge_kernel(FullDev full, __bf1
 
 template <int D, int MODE>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  if constexpr (fwd_pair_dispatch<D, MODE>()) {
+    constexpr int BR = PairFwd<D>::BR;
+    const int nqb = (p.n + BR - 1) / BR;
+    const long total = (long)nqb * p.B * p.H;
+    if (total > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fwd_pair_kernel<D, MODE>), dim3((unsigned)total), dim3(PairFwd<D>::NT), 0, stream,
+                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (__bf16*)p.o, p.lse, p.n, nqb,
+                       (int)total, p.scale * kLog2e, p.window, p.group);
+    return hipGetLastError();
+  }
   constexpr int BR = 32 * FwdCfg<D>::RB * fwd_waves<D, MODE>();
   const int nqb = (p.n + BR - 1) / BR;
   const long total = (long)nqb * p.B * p.H;
@@ -564,7 +825,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     if (e != hipSuccess || p.full.idx == nullptr) return e;
     return launch_mode<kMaskFull>(p, stream);
   }
-  if (p.window < 0 && p.d == 256) {
+  if (!fwd_pair_dispatch<256, kMaskNone>() && p.window < 0 && p.d == 256) {
     // The two-waves-per-SIMD d=256 kernel only pays once every CU holds two
     // of its workgroups; smaller grids run the one-wave kernel, reached as a
     // window of n (every key visible; only the ragged tail tile is masked).

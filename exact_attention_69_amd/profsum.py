@@ -46,12 +46,13 @@ def kernel_source_sha256(kernel=None):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
-KERNEL_RE = re.compile(r"(fwd_bf16_kernel|bwd_kv_bf16_kernel|bwd_q_bf16_kernel|bwd_rowdot_kernel|fwd_f32_kernel|"
+KERNEL_RE = re.compile(r"(fwd_bf16_kernel|fwd_pair_kernel|bwd_kv_bf16_kernel|bwd_kv_pair_kernel|bwd_q_bf16_kernel|"
+                       r"bwd_rowdot_kernel|fwd_f32_kernel|"
                        r"bwd_kv_f32_kernel|bwd_q_f32_kernel|pattern_bitmap_kernel|pattern_list_kernel|"
                        r"pattern_layout_full_kernel|pattern_gather_kernel|fwd_full_merge_kernel|full_sum_kernel|fwd_fp8_kernel|"
                        r"quant_\w+?kernel|"
                        r"elementwise_kernel|copy\w*)(I\w*?E(?:EvP|Ev$|EEv))?")
-# mask mode (second template argument of the bf16 kernels); the unmasked one is unnamed
+# mask mode (second template argument of the bf16 and paired kernels); the unmasked one is unnamed
 MODE_NAMES = {"1": "window", "2": "pattern", "3": "full"}
 
 
@@ -66,7 +67,7 @@ def short(name):
     if not args:
         return m.group(1)
     label = args[0]
-    if len(args) > 1 and m.group(1).endswith("bf16_kernel") and args[1] in MODE_NAMES:
+    if len(args) > 1 and m.group(1).endswith(("bf16_kernel", "pair_kernel")) and args[1] in MODE_NAMES:
         label += "," + MODE_NAMES[args[1]]
     elif len(args) > 1 and m.group(1) == "full_sum_kernel":
         label += "," + args[1]

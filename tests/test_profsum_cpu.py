@@ -47,3 +47,22 @@ def test_measured_traffic_refuses_stale_and_foreign_records(tmp_path, monkeypatc
     assert bench.measured_traffic(wl, kernel) is None
     write("bf16_b4h16_n2048_d64", profsum.kernel_source_sha256(kernel))  # another workload
     assert bench.measured_traffic(wl, kernel) is None
+
+
+def test_paired_kernels_are_named_like_the_others():
+    mangled = {
+        "_ZN6exattn12_GLOBAL__N_118bwd_kv_pair_kernelILi128ELi0EEEvPKDF16bS3_S3_S3_PKfS5_PDF16bS6_iiiffii":
+            "bwd_kv_pair_kernel<128>",
+        "_ZN6exattn12_GLOBAL__N_118bwd_kv_pair_kernelILi256ELi1EEEvPKDF16bS3_S3_S3_PKfS5_PDF16bS6_iiiffii":
+            "bwd_kv_pair_kernel<256,window>",
+        "_ZN6exattn12_GLOBAL__N_115fwd_pair_kernelILi256ELi1EEEvPKDF16bS3_S3_PDF16bPfiiifii":
+            "fwd_pair_kernel<256,window>",
+    }
+    for name, short in mangled.items():
+        assert profsum.short(name) == short
+    assert "bwd_bf16.hip" in _names(profsum.kernel_sources("bwd_kv_pair_kernel<128>"))
+    assert "fwd_bf16.hip" in _names(profsum.kernel_sources("fwd_pair_kernel<256,window>"))
+    # the bench's names of a step follow the dispatch
+    assert bench.kernel_names(workload("bf16_b2h32_n8192_d128_q3"))[2] == "bwd_kv_pair_kernel<128>"
+    c5 = bench.kernel_names(workload("bf16_b2h8_n16384_d256_w512"))
+    assert c5[0] == "fwd_pair_kernel<256,window>" and c5[2] == "bwd_kv_pair_kernel<256,window>"
