@@ -124,16 +124,17 @@ def cpu_baseline(wl, seconds):
 
 def kernel_names(wl):
     """Short names (as the profile summaries write them) of the four kernels
-    of a step: forward, rowdot, dK/dV, dQ.  In bf16 the forward at d = 256
-    and the dK/dV pass at d = 256, and at d = 128 without a window, run on
-    the paired-wave kernels."""
+    of a step: forward, rowdot, dK/dV, dQ.  In bf16 the forward and the dQ
+    pass at d = 256 and the dK/dV pass at d = 256, and at d = 128 without a
+    window, run on the paired-wave kernels."""
     t, d = wl.dtype, wl.d
     if t != "bf16":
         return [f"fwd_{t}_kernel<{d}>", f"bwd_rowdot_kernel<{d}>", f"bwd_kv_{t}_kernel<{d}>", f"bwd_q_{t}_kernel<{d}>"]
     m = ",window" if wl.window >= 0 else ""
     fwd = "fwd_pair_kernel" if d == 256 else "fwd_bf16_kernel"
     kv = "bwd_kv_pair_kernel" if d == 256 or (d == 128 and wl.window < 0) else "bwd_kv_bf16_kernel"
-    return [f"{fwd}<{d}{m}>", f"bwd_rowdot_kernel<{d}>", f"{kv}<{d}{m}>", f"bwd_q_bf16_kernel<{d}{m}>"]
+    dq = "bwd_q_pair_kernel" if d == 256 else "bwd_q_bf16_kernel"
+    return [f"{fwd}<{d}{m}>", f"bwd_rowdot_kernel<{d}>", f"{kv}<{d}{m}>", f"{dq}<{d}{m}>"]
 
 
 def time_steps(wl, steps, warmup, graph=False):

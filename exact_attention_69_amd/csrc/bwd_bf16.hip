@@ -1103,6 +1103,211 @@ __global__ __launch_bounds__(256) void full_sum_kernel(FullDev full, __bf16* __r
   }
 }
 
+// ---------------------------------------------------------------------------
+// Query side at d = 256 without a pattern: paired waves.
+// ---------------------------------------------------------------------------
+// The 8 waves form 4 pairs (wave w and wave w+4 share a SIMD); a pair owns 32
+// query rows.  The dS-wave holds the rows' Q in registers and their dO rows
+// in LDS and, per key tile, forms S = Q K^T and dP = dO V^T, then
+// dS = P (dP - D) with P = exp(S - LSE), and hands dS (bf16 MFMA operands)
+// to its partner through LDS; the dQ-wave holds the dQ accumulator and adds
+// dS K, one tile behind.  One wave holding Q, dO and dQ needed all 512
+// registers of a SIMD; split this way the SIMD runs two waves, each one's
+// latencies covered by the other's work.  K tiles stay in LDS one iteration
+// longer than V tiles (the dQ-wave reads tile i-1 while the dS-wave reads
+// tile i): three K buffers, two V buffers; with the dO rows they fill the
+// 160 KiB of LDS.
+template <int D>
+struct PairQ {
+  static constexpr int BC = 32, NT = 512, BR = 128;
+  static constexpr int kTile = BC * D * 2;       // bytes of one K or V tile
+  static constexpr int kK = 0;                   // [3] K tiles
+  static constexpr int kV = kK + 3 * kTile;      // [2] V tiles
+  static constexpr int kSPair = 2 * 64 * 16;     // one pair's dS operands
+  static constexpr int kS = kV + 2 * kTile;      // [2][pair]
+  static constexpr int kGPair = 32 * D * 2;      // one pair's dO rows
+  static constexpr int kG = kS + 2 * 4 * kSPair; // [pair]
+  static constexpr int kBytes = kG + 4 * kGPair;
+  static_assert(kBytes <= 160 * 1024, "one workgroup per CU");
+};
+
+template <int D, int MODE>
+constexpr bool pair_q_dispatch() {
+  return D == 256 && (MODE == kMaskNone || MODE == kMaskWindow);
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(512, 2) void bwd_q_pair_kernel(
+    const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
+    const __bf16* __restrict__ dOg, const float* __restrict__ LSE2g, const float* __restrict__ Dg,
+    __bf16* __restrict__ dQg, int n, int n_qblocks, int total_blocks, float scale, float scale_log2, int window,
+    int group) {
+  using C = PairQ<D>;
+  constexpr bool WINDOWED = MODE == kMaskWindow;
+  constexpr int BC = C::BC, NT = C::NT, BR = C::BR;
+  constexpr int NDS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) char lds[C::kBytes];
+  poison_lds(lds);
+
+  const int bid = xcd_remap(blockIdx.x, total_blocks);
+  const int head = bid / n_qblocks;
+  const int qb = bid - head * n_qblocks;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const bool swave = wave < 4;  // dS-wave, else dQ-wave
+
+  const size_t hoff = (size_t)head * n * D;
+  const size_t kv_off = (size_t)(head / group) * n * D;  // key/value head of this query head
+  const __bf16* K = Kg + kv_off;
+  const __bf16* V = Vg + kv_off;
+  const int q0 = qb * BR;
+  const int w0 = q0 + pair * 32;  // first row of the pair
+  const int my_row = w0 + l32;
+
+  int k_lo = 0, k_hi = n;
+  if constexpr (WINDOWED) band_keys(q0, q0 + BR, n, window, &k_lo, &k_hi);
+  const int t_lo = k_lo / BC;
+  const int n_tiles = (k_hi + BC - 1) / BC - t_lo;
+
+  // K and V tiles go straight from global memory to LDS.  Key rows past n
+  // are zeros in the K tile, so whatever their dS, they add exactly nothing
+  // to dQ = dS K (their V rows are clamped copies and only feed that dS).
+  using Tile = TileAsync<D, BC, NT>;
+  using TileK = TileAsyncZeroTail<D, BC, NT>;
+  using Dma = TileDma<D, BC, NT>;
+  uint32_t dma_off[Dma::IT];
+  Dma::init(tid, dma_off);
+  auto load_tile = [&](int i) {
+    const int kbase = (t_lo + i) * BC;
+    __bf16* kd = (__bf16*)(lds + C::kK + (i % 3) * C::kTile);
+    __bf16* vd = (__bf16*)(lds + C::kV + (i & 1) * C::kTile);
+    if (kbase + BC <= n) {
+      Dma::issue(K + (size_t)kbase * D, dma_off, kd, wave);
+      Dma::issue(V + (size_t)kbase * D, dma_off, vd, wave);
+    } else {
+      TileK::issue(K + (size_t)kbase * D, n - kbase, kd, tid);
+      Tile::issue(V + (size_t)kbase * D, n - kbase, vd, tid);
+    }
+  };
+  // a pair skips the key tiles its rows' band misses
+  auto pair_sees = [&](int i) -> bool {
+    if constexpr (WINDOWED) {
+      const int c0 = (t_lo + i) * BC;
+      return c0 <= w0 + 31 + window && w0 <= c0 + BC - 1 + window;
+    } else {
+      return true;
+    }
+  };
+  const int s_off = C::kS + pair * C::kSPair + 16 * lane;  // + buffer * 4 * kSPair + operand * 1024
+
+  // The dS-wave's Q^T operands (lane: row my_row, columns 16*ds + 8*hi ..
+  // +8), its row's LSE*log2(e) and -D, and its dO rows (to LDS, swizzled like
+  // the tiles; rows past n are clamped copies), loaded before the first
+  // wait, which then covers them (the compiler's own wait for these loads
+  // would otherwise sit inside the loop and also wait for the copies issued
+  // there).
+  const int g_base = C::kG + pair * C::kGPair;  // wave-uniform
+  bf16x8 qreg[NDS];
+  float lse2 = 0.0f, ndl = 0.0f;
+  if (swave) {
+    const bool ok = my_row < n;
+    const u32x4* qs = (const u32x4*)(Qg + hoff + (size_t)(ok ? my_row : 0) * D + 8 * hi);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qreg[ds] = __builtin_bit_cast(bf16x8, ok ? qs[2 * ds] : u32x4{0, 0, 0, 0});
+    lse2 = ok ? LSE2g[(size_t)head * n + my_row] : __builtin_huge_valf();  // rows past n: P = 0
+    ndl = ok ? Dg[(size_t)head * n + my_row] : 0.0f;
+#pragma unroll
+    for (int it = 0; it < 32 * (D / 8) / 64; ++it) {
+      const int slot = it * 64 + lane, row = slot / (D / 8);
+      const int r = min(w0 + row, n - 1);
+      lds_dma16(dOg + hoff + (size_t)r * D + 8 * swz_chunk<D>(row, slot % (D / 8)), lds + g_base + 16 * (it * 64));
+    }
+  }
+  if (n_tiles > 0) load_tile(0);
+  wait_all_and_barrier();
+
+  if (swave) {
+    // keys this lane's row sees: [key_lo, key_lo + key_span)
+    int key_lo = 0, key_hi = n;
+    if constexpr (WINDOWED) band_keys(my_row, my_row + 1, n, window, &key_lo, &key_hi);
+    const unsigned key_span = (unsigned)max(key_hi - key_lo, 0);
+    for (int i = 0; i <= n_tiles; ++i) {
+      if (i + 1 < n_tiles) load_tile(i + 1);
+      if (i < n_tiles && pair_sees(i)) {
+        const __bf16* Ks = (const __bf16*)(lds + C::kK + (i % 3) * C::kTile);
+        const __bf16* Vs = (const __bf16*)(lds + C::kV + (i & 1) * C::kTile);
+        const int kbase = (t_lo + i) * BC;
+        // S^T = K Q^T and dP^T = V dO^T: lanes = the pair's rows, registers
+        // = keys; the dP accumulator starts at the row's -D, so the product
+        // ends as dP - D
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = ndl;
+        const __bf16* Gs = (const __bf16*)(lds + g_base);
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+          s = mfma32(lds_row_frag<D>(Ks, l32, ds, hi), qreg[ds], s);
+          dp = mfma32(lds_row_frag<D>(Vs, l32, ds, hi), lds_row_frag<D>(Gs, l32, ds, hi), dp);
+        }
+        // P = 2^(scale*log2e*s - LSE*log2e) (keys outside the row's band,
+        // and past n, get P = 0), dS^T = P^T (dP^T - D) (unscaled)
+        bool need_mask = kbase + BC > n;
+        if constexpr (WINDOWED) need_mask = need_mask || max(w0 + 31 - kbase, kbase + BC - 1 - w0) > window;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lse2));
+          if (need_mask) {
+            const int key = kbase + acc_row(r, lane);
+            p = (unsigned)(key - key_lo) < key_span ? p : 0.0f;
+          }
+          dp[r] *= p;
+        }
+        // to the dQ-wave: lane-private 16-byte slots, consecutive lanes in
+        // consecutive slots
+        const int b = i & 1;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          *(u32x4*)(lds + s_off + b * (4 * C::kSPair) + c * 1024) = __builtin_bit_cast(u32x4, acc_to_operand(dp, c));
+      }
+      wait_all_and_barrier();
+    }
+  } else {
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
+    for (int i = 0; i <= n_tiles; ++i) {
+      if (i + 1 < n_tiles) load_tile(i + 1);
+      if (i >= 1 && pair_sees(i - 1)) {
+        const int b = (i - 1) & 1;
+        const __bf16* Ks = (const __bf16*)(lds + C::kK + ((i - 1) % 3) * C::kTile);
+        // dQ^T += K^T dS^T, k along the tile's keys (K^T through the
+        // transpose read)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 sb = *(const bf16x8*)(lds + s_off + b * (4 * C::kSPair) + st * 1024);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dq[db] = mfma32(lds_col_frag<D>(Ks, 16 * st, 32 * db, lane), sb, dq[db]);
+        }
+      }
+      wait_all_and_barrier();
+    }
+    if (my_row < n) {
+      __bf16* dqr = dQg + hoff + (size_t)my_row * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dd = 32 * db + 8 * g + 4 * hi;
+          u32x2 w;
+          w[0] = pack_bf16x2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
+          w[1] = pack_bf16x2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+          *(u32x2*)(dqr + dd) = w;
+        }
+    }
+  }
+}
+
 // Key side, then query side, of one mask mode.
 template <int D, int W>
 hipError_t bwd_passes(const BwdParams& p, unsigned stages, hipStream_t stream) {
@@ -1139,10 +1344,17 @@ hipError_t bwd_passes(const BwdParams& p, unsigned stages, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stages & kStageQ) {
-    hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(q_waves<D, W>() * 64), 0, stream,
-                       (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
-                       p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group, pq,
-                       p.full_q);
+    if constexpr (pair_q_dispatch<D, W>()) {
+      static_assert(BR == PairQ<D>::BR, "the paired kernel's row block matches the grid");
+      hipLaunchKernelGGL((bwd_q_pair_kernel<D, W>), dim3((unsigned)tq), dim3(PairQ<D>::NT), 0, stream,
+                         (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
+                         p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group);
+    } else {
+      hipLaunchKernelGGL((bwd_q_bf16_kernel<D, W>), dim3((unsigned)tq), dim3(q_waves<D, W>() * 64), 0, stream,
+                         (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (const __bf16*)p.dout, p.lse2,
+                         p.delta, (__bf16*)p.dq, p.n, nqb, (int)tq, p.scale, scale_log2, p.window, p.group, pq,
+                         p.full_q);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && W == kMaskFull) {
       hipLaunchKernelGGL((full_sum_kernel<D, 1>), dim3(1024), dim3(256), 0, stream, p.full_q, (__bf16*)p.dq,

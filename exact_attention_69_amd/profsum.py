@@ -47,6 +47,7 @@ def kernel_source_sha256(kernel=None):
     return h.hexdigest()
 
 KERNEL_RE = re.compile(r"(fwd_bf16_kernel|fwd_pair_kernel|bwd_kv_bf16_kernel|bwd_kv_pair_kernel|bwd_q_bf16_kernel|"
+                       r"bwd_q_pair_kernel|"
                        r"bwd_rowdot_kernel|fwd_f32_kernel|"
                        r"bwd_kv_f32_kernel|bwd_q_f32_kernel|pattern_bitmap_kernel|pattern_list_kernel|"
                        r"pattern_layout_full_kernel|pattern_gather_kernel|fwd_full_merge_kernel|full_sum_kernel|fwd_fp8_kernel|"

@@ -57,6 +57,8 @@ def test_paired_kernels_are_named_like_the_others():
             "bwd_kv_pair_kernel<256,window>",
         "_ZN6exattn12_GLOBAL__N_115fwd_pair_kernelILi256ELi1EEEvPKDF16bS3_S3_PDF16bPfiiifii":
             "fwd_pair_kernel<256,window>",
+        "_ZN6exattn12_GLOBAL__N_117bwd_q_pair_kernelILi256ELi0EEEvPKDF16bS3_S3_S3_PKfS5_PDF16biiiffii":
+            "bwd_q_pair_kernel<256>",
     }
     for name, short in mangled.items():
         assert profsum.short(name) == short
@@ -66,3 +68,4 @@ def test_paired_kernels_are_named_like_the_others():
     assert bench.kernel_names(workload("bf16_b2h32_n8192_d128_q3"))[2] == "bwd_kv_pair_kernel<128>"
     c5 = bench.kernel_names(workload("bf16_b2h8_n16384_d256_w512"))
     assert c5[0] == "fwd_pair_kernel<256,window>" and c5[2] == "bwd_kv_pair_kernel<256,window>"
+    assert c5[3] == "bwd_q_pair_kernel<256,window>"
