@@ -66,21 +66,6 @@ constexpr int fwd_waves() {
   return MODE == kMaskFull ? kFullRows / 32 : MODE == kMaskPattern ? 4 : FwdCfg<D>::NW;
 }
 
-// Without a mask, d=256 runs two waves per SIMD: its next-tile scores are
-// then formed after the P V product (one score tile live instead of two), and
-// 6 of the 16 Q operand registers spill, yet the second wave more than pays
-// for it (0.818 -> 0.715 ms at n=8192, 8 heads).  With a window the masked
-// edge tiles tip it the other way (0.596 -> 0.638 ms), so there the kernel
-// keeps one wave per SIMD and the pipelined scores.
-template <int D, int MODE>
-constexpr bool fwd_two_waves_d256() {
-  return D == 256 && MODE == kMaskNone;
-}
-template <int D, int MODE>
-constexpr int fwd_wpe() {
-  return fwd_two_waves_d256<D, MODE>() ? 2 : FwdCfg<D>::WPE;
-}
-
 // MODE: kMaskNone, kMaskWindow (contiguous band of key tiles, analytic
 // masks), kMaskPattern (the workgroup's tile list from the pattern plan; the
 // union mask on partial tiles; full rows are left to the full-row pass), or
@@ -88,7 +73,7 @@ constexpr int fwd_wpe() {
 // with several chunks the normalised partial O and its log-sum-exp go to the
 // partial buffers).
 template <int D, int MODE>
-__global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) void fwd_bf16_kernel(
+__global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), FwdCfg<D>::WPE) void fwd_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     __bf16* __restrict__ Og, float* __restrict__ LSEg, int n, int n_qblocks, int total_blocks,
     float scale_log2, int window, int group, PatternDev pat, FullDev full) {
@@ -288,7 +273,6 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) 
     }
   };
 
-  constexpr bool kPipeS = !fwd_two_waves_d256<D, MODE>();  // next tile's S beside the exponentials
   f32x16 s_cur[RB][NKB];
   bool act_cur = !PATTERN || (n_tiles > 0 && wave_sees(0));
   if (act_cur) compute_s(kbuf[0], s_cur);
@@ -407,7 +391,7 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) 
           pb[rb][2 * kb] = acc_to_operand(s_cur[rb][kb], 0);
           pb[rb][2 * kb + 1] = acc_to_operand(s_cur[rb][kb], 1);
         }
-        if (kPipeS && act_next) compute_s_block(kbuf[(j + 1) & 1], kb, s_cur);
+        if (act_next) compute_s_block(kbuf[(j + 1) & 1], kb, s_cur);
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) l_part[rb] += (lsum[rb][0] + lsum[rb][1]) + (lsum[rb][2] + lsum[rb][3]);
@@ -433,7 +417,6 @@ __global__ __launch_bounds__((fwd_waves<D, MODE>() * 64), (fwd_wpe<D, MODE>())) 
           if (i + kLead < NP) EXATTN_SCHED(kSchedDSRead, 2);
         }
       }
-      if (!kPipeS && act_next) compute_s(kbuf[(j + 1) & 1], s_cur);
     } else if (act_next) {
       compute_s(kbuf[(j + 1) & 1], s_cur);
     }
@@ -774,6 +757,10 @@ __global__ __launch_bounds__(256) void fwd_full_merge_kernel(FullDev full, __bf1
   }
 }
 
+// The kernels of the modes the paired kernel does not take.
+template <int D, int MODE>
+hipError_t launch_d_main(const FwdParams& p, hipStream_t stream);
+
 template <int D, int MODE>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   if constexpr (fwd_pair_dispatch<D, MODE>()) {
@@ -785,7 +772,13 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
                        (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, (__bf16*)p.o, p.lse, p.n, nqb,
                        (int)total, p.scale * kLog2e, p.window, p.group);
     return hipGetLastError();
+  } else {
+    return launch_d_main<D, MODE>(p, stream);
   }
+}
+
+template <int D, int MODE>
+hipError_t launch_d_main(const FwdParams& p, hipStream_t stream) {
   constexpr int BR = 32 * FwdCfg<D>::RB * fwd_waves<D, MODE>();
   const int nqb = (p.n + BR - 1) / BR;
   const long total = (long)nqb * p.B * p.H;
@@ -824,18 +817,6 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     if (e == hipSuccess) e = launch_mode<kMaskPattern>(p, stream);
     if (e != hipSuccess || p.full.idx == nullptr) return e;
     return launch_mode<kMaskFull>(p, stream);
-  }
-  if (!fwd_pair_dispatch<256, kMaskNone>() && p.window < 0 && p.d == 256) {
-    // The two-waves-per-SIMD d=256 kernel only pays once every CU holds two
-    // of its workgroups; smaller grids run the one-wave kernel, reached as a
-    // window of n (every key visible; only the ragged tail tile is masked).
-    constexpr int kRows = 32 * FwdCfg<256>::RB * FwdCfg<256>::NW;
-    const long blocks = (long)((p.n + kRows - 1) / kRows) * p.B * p.H;
-    if (blocks < 2L * device_cu_count(stream)) {
-      FwdParams q = p;
-      q.window = p.n;
-      return launch_mode<kMaskWindow>(q, stream);
-    }
   }
   return p.window >= 0 ? launch_mode<kMaskWindow>(p, stream) : launch_mode<kMaskNone>(p, stream);
 }

@@ -8,25 +8,6 @@
 
 namespace exattn {
 
-// Compute units of the current device, queried once per device (256 on
-// MI355X, which is also the answer when the query fails, and before the
-// first query if `stream` is being captured into a graph: no device query is
-// made during a capture).
-inline int device_cu_count(hipStream_t stream) {
-  constexpr int kMaxDev = 64;
-  static int cache[kMaxDev] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
-  int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-  if (c == 0) {
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return 256;
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    __atomic_store_n(&cache[dev], c, __ATOMIC_RELAXED);
-  }
-  return c;
-}
-
 // Masking modes of the kernels.
 // kMaskFull: the full positions of a pattern (rows or keys gathered from the
 // plan's list), each workgroup over one chunk of the other side's tiles.

@@ -102,7 +102,7 @@ def test_fp8_step_in_a_graph():
 
 
 def test_dense_d256_forward_on_a_large_grid_in_a_graph():
-    """The two-waves-per-SIMD d=256 forward (a grid of 512 workgroups)."""
+    """The paired-wave d=256 forward (a grid of 512 workgroups)."""
     import exact_attention_69_amd as ea
     wl = make_case(2, 16, 2048, 256, "bf16", seed=4)
     static = to_device(draw_inputs(wl, ("q", "k", "v")), "bf16")
