@@ -51,34 +51,72 @@ __host__ __device__ inline int vt_column(int k) {
 // ---------------------------------------------------------------------------
 // Quantiser
 // ---------------------------------------------------------------------------
-// One wave per row, EPL = d / 64 elements per lane: element i = lane + 64*e.
-template <int D>
-__device__ __forceinline__ void load_rotated_row(const __bf16* __restrict__ row, const float* __restrict__ signs,
-                                                 int lane, float (&x)[D / 64]) {
-  constexpr int EPL = D / 64;
+// Rows in the row-group layout: the G = D/8 consecutive lanes of a group
+// hold one row, 8 consecutive elements each (element i = 8*l + j,
+// l = lane % G): one 16-byte load per lane.  The rotation's butterfly stages
+// run in the order h = 1, 2, 4 (within the lane), then h = 8 .. D/2 (across
+// the group's lanes, by shuffles); each stage forms lower + upper and
+// lower - upper of its pairs.
+// x of the lane whose index differs from this lane's in bit log2(M) (M = 1,
+// 2, 4, 8: within a row of 16 lanes), by DPP moves (vector ALU, no LDS):
+// XOR 1 and 2 are quad permutations; XOR 4 = XOR 3 (reverse the quad) then
+// the mirror of each 8 lanes (XOR 7); XOR 8 = XOR 7 then the mirror of the
+// row of 16 (15 - i).
+template <int M>
+__device__ __forceinline__ float lanes_xor(float x) {
+  constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadRev = 0x1B, kHalfMirror = 0x141, kMirror = 0x140;
+  int v = __builtin_bit_cast(int, x);
+  if constexpr (M == 1) {
+    v = __builtin_amdgcn_mov_dpp(v, kQuadXor1, 0xF, 0xF, true);
+  } else if constexpr (M == 2) {
+    v = __builtin_amdgcn_mov_dpp(v, kQuadXor2, 0xF, 0xF, true);
+  } else if constexpr (M == 4) {
+    v = __builtin_amdgcn_mov_dpp(v, kQuadRev, 0xF, 0xF, true);
+    v = __builtin_amdgcn_mov_dpp(v, kHalfMirror, 0xF, 0xF, true);
+  } else {
+    static_assert(M == 8, "partners within a row of 16 lanes");
+    v = __builtin_amdgcn_mov_dpp(v, kHalfMirror, 0xF, 0xF, true);
+    v = __builtin_amdgcn_mov_dpp(v, kMirror, 0xF, 0xF, true);
+  }
+  return __builtin_bit_cast(float, v);
+}
+
+template <int D, int M>
+__device__ __forceinline__ void butterfly_across(float (&x)[8], int l) {
+  // lower lane: x + b; upper lane: b - x; one fma with a sign, exact
+  // before its one rounding, so the same value as the add or subtract
+  const float sg = (l & M) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) x[e] = (float)row[lane + 64 * e];
+  for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(sg, x[j], lanes_xor<M>(x[j]));
+  if constexpr (8 * 2 * M < D) butterfly_across<D, 2 * M>(x, l);
+}
+
+template <int D>
+__device__ __forceinline__ void rotate_row8(const u32x4& w, const float* __restrict__ signs, int l, float (&x)[8]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    x[2 * t] = __builtin_bit_cast(float, w[t] << 16);
+    x[2 * t + 1] = __builtin_bit_cast(float, w[t] & 0xffff0000u);
+  }
   if (signs == nullptr) return;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) x[e] *= signs[lane + 64 * e];
-  // stages h = 1 .. 32 across lanes, then h = 64 (and 128) within the lane
+  for (int j = 0; j < 8; ++j) x[j] *= signs[8 * l + j];
 #pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
+  for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float b = __shfl_xor(x[e], h, 64);
-      x[e] = (lane & h) ? b - x[e] : x[e] + b;
-    }
-  }
-#pragma unroll
-  for (int h = 1; h < EPL; h <<= 1)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      if ((e & h) == 0) {
-        const float a = x[e], b = x[e + h];
-        x[e] = a + b;
-        x[e + h] = a - b;
+    for (int j = 0; j < 8; ++j)
+      if ((j & h) == 0) {
+        const float a = x[j], b = x[j + h];
+        x[j] = a + b;
+        x[j + h] = a - b;
       }
+  butterfly_across<D, 1>(x, l);  // h = 8, 16, .., D/2: partner lane l ^ (h/8)
+}
+
+template <int D>
+__device__ __forceinline__ void load_rotated_row8(const __bf16* __restrict__ row, const float* __restrict__ signs,
+                                                  int l, float (&x)[8]) {
+  rotate_row8<D>(*(const u32x4*)(row + 8 * l), signs, l, x);
 }
 
 __global__ __launch_bounds__(256) void quant_clear_kernel(uint32_t* __restrict__ amax_bits, int heads) {
@@ -87,70 +125,131 @@ __global__ __launch_bounds__(256) void quant_clear_kernel(uint32_t* __restrict__
 }
 
 // amax of every head: |x| as uint bits (monotonic for non-negative floats).
-// A workgroup reduces kAmaxRows rows of one head (its four waves take every
-// fourth row) in registers, then across its waves in LDS, and issues one
-// atomic max: a head's rows meet at one address n / kAmaxRows times instead
-// of once per row.
-constexpr int kAmaxRows = 64;
+// A workgroup reduces kAmaxRows rows of one head in registers, then across
+// its waves in LDS, and issues one atomic max: a head's rows meet at one
+// address n / kAmaxRows times.  (Atomics on one address are served one after
+// another, about half a microsecond each: 64 rows per workgroup took
+// 0.075 ms for a 128 MiB tensor, 512 take a fraction of that.)
+constexpr int kAmaxRows = 512;
+
+constexpr int kAmaxWaves = 16;  // waves per workgroup: enough of them to cover the rotation's latencies
 
 template <int D>
-__global__ __launch_bounds__(256) void quant_amax_kernel(const __bf16* __restrict__ X, const float* __restrict__ signs,
-                                                        uint32_t* __restrict__ amax_bits, int n, int chunks) {
-  __shared__ float wave_max[4];
+__global__ __launch_bounds__(kAmaxWaves * 64) void quant_amax_kernel(const __bf16* __restrict__ X,
+                                                                     const float* __restrict__ signs,
+                                                                     uint32_t* __restrict__ amax_bits, int n,
+                                                                     int chunks) {
+  constexpr int G = D / 8, RPW = 64 / G, NW = kAmaxWaves;  // lanes per row, rows per wave
+  __shared__ float wave_max[NW];
   poison_lds(wave_max);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long head = blockIdx.x / chunks;
   const int r0 = (int)(blockIdx.x - head * chunks) * kAmaxRows;
   const int r1 = min(r0 + kAmaxRows, n);
   float m = 0.0f;
-  for (int r = r0 + wave; r < r1; r += 4) {
-    float x[D / 64];
-    load_rotated_row<D>(X + (head * n + r) * D, signs, lane, x);
+  // Batches of BATCH passes; in pass p a lane takes row
+  // r0 + wave*RPW + lane/G + NW*RPW*p.  A batch's rows are all loaded before
+  // any is processed (every lane of a row group takes the same rows, so the
+  // group's shuffles stay among active lanes; rows past r1 read as zeros,
+  // which leave the max alone).
+  constexpr int BATCH = kAmaxRows / (NW * RPW) < 8 ? kAmaxRows / (NW * RPW) : 8, PER_BATCH = NW * RPW * BATCH;
+  static_assert(kAmaxRows % PER_BATCH == 0, "whole batches per workgroup");
+  const int l = lane % G;
+  for (int b0 = r0; b0 < r1; b0 += PER_BATCH) {
+    u32x4 raw[BATCH];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) m = fmaxf(m, fabsf(x[e]));
+    for (int p = 0; p < BATCH; ++p) {
+      const int r = b0 + wave * RPW + lane / G + NW * RPW * p;
+      raw[p] = r < r1 ? *(const u32x4*)(X + (head * n + r) * D + 8 * l) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int p = 0; p < BATCH; ++p) {
+      float x[8];
+      rotate_row8<D>(raw[p], signs, l, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+    }
   }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
   if (lane == 0) wave_max[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float w = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    float w = wave_max[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) w = fmaxf(w, wave_max[i]);
     atomicMax(&amax_bits[head], __float_as_uint(w));
   }
 }
 
-// codes; `transposed`: write the V layout described at the top; rows
-// n .. n128-1 of a head write zero columns there.
+// Codes of the row layout, in the row-group layout: each lane converts and
+// stores its 8 codes as one 8-byte word.
 template <int D>
-__global__ __launch_bounds__(256) void quant_codes_kernel(const __bf16* __restrict__ X,
-                                                         const float* __restrict__ signs,
-                                                         const uint32_t* __restrict__ amax_bits,
-                                                         uint8_t* __restrict__ X8, int n, int n128, long heads,
-                                                         int transposed) {
-  const int lane = threadIdx.x & 63;
-  const long prow = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // row in [heads * rows_per_head)
-  const int rows_per_head = transposed ? n128 : n;
-  if (prow >= heads * rows_per_head) return;
-  const long head = prow / rows_per_head;
-  const int r = (int)(prow - head * rows_per_head);
-  float x[D / 64];
-  if (r < n) {
-    load_rotated_row<D>(X + (head * n + r) * D, signs, lane, x);
-  } else {
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) x[e] = 0.0f;
-  }
+__global__ __launch_bounds__(256) void quant_codes_rows_kernel(const __bf16* __restrict__ X,
+                                                              const float* __restrict__ signs,
+                                                              const uint32_t* __restrict__ amax_bits,
+                                                              uint8_t* __restrict__ X8, int n, long rows) {
+  constexpr int G = D / 8, RPB = 256 / G;  // lanes per row, rows per workgroup
+  const int l = threadIdx.x % G;
+  const long prow = (long)blockIdx.x * RPB + threadIdx.x / G;  // row in [heads * n)
+  if (prow >= rows) return;  // whole row groups (G divides 64)
+  const long head = prow / n;
+  float x[8];
+  load_rotated_row8<D>(X + prow * D, signs, l, x);
   const float amax = __uint_as_float(amax_bits[head]);
   const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
+  float q[8];
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) {
-    const float q = fminf(fmaxf(x[e] * inv, -kE4M3Max), kE4M3Max);
-    const uint8_t code = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xff);
-    const int i = lane + 64 * e;
-    if (transposed)
-      X8[(head * D + i) * n128 + vt_column(r)] = code;
-    else
-      X8[(head * n + r) * D + i] = code;
+  for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(x[j] * inv, -kE4M3Max), kE4M3Max);
+  u32x2 w;
+  w[0] = (uint32_t)pack_e4m3x4(q[0], q[1], q[2], q[3]);
+  w[1] = (uint32_t)pack_e4m3x4(q[4], q[5], q[6], q[7]);
+  *(u32x2*)(X8 + prow * D + 8 * l) = w;
+}
+
+// Codes of the transposed V layout: a workgroup takes one 64-key group of a
+// head, converts its rows in the row-group layout, transposes the codes
+// through LDS (row stride 68 bytes, so that the byte writes of a row
+// group's lanes spread over the banks) and writes each of the D output rows'
+// 64 columns as four 16-byte words.  Keys at or beyond n give zero columns.
+template <int D>
+__global__ __launch_bounds__(256) void quant_codes_t_kernel(const __bf16* __restrict__ X,
+                                                           const float* __restrict__ signs,
+                                                           const uint32_t* __restrict__ amax_bits,
+                                                           uint8_t* __restrict__ X8, int n, int n128, int groups) {
+  constexpr int G = D / 8, RPP = 256 / G;  // lanes per row, rows per pass
+  constexpr int RS = 68;                  // LDS bytes per output row
+  __shared__ __attribute__((aligned(16))) uint32_t t[D * RS / 4];
+  poison_lds(t);
+  const long head = blockIdx.x / groups;
+  const int k0 = (int)(blockIdx.x - head * groups) * 64;
+  const int tid = threadIdx.x, l = tid % G;
+  const float amax = __uint_as_float(amax_bits[head]);
+  const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
+  uint8_t* tb = (uint8_t*)t;
+#pragma unroll
+  for (int p = 0; p < 64 / RPP; ++p) {
+    const int k = k0 + p * RPP + tid / G;  // key (row of X); groups of G lanes share it
+    float x[8];
+    if (k < n) {
+      load_rotated_row8<D>(X + (head * n + k) * D, signs, l, x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.0f;
+    }
+    const int c = vt_column(k - k0);  // column within the group
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float q = fminf(fmaxf(x[j] * inv, -kE4M3Max), kE4M3Max);
+      tb[(8 * l + j) * RS + c] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xff);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < D * 4 / 256; ++q) {
+    const int chunk = tid + 256 * q, i = chunk >> 2, part = chunk & 3;
+    const uint32_t* src = t + (i * RS + 16 * part) / 4;
+    *(u32x4*)(X8 + ((size_t)head * D + i) * n128 + k0 + 16 * part) = u32x4{src[0], src[1], src[2], src[3]};
   }
 }
 
@@ -382,18 +481,27 @@ hipError_t launch_quant_fp8(const Fp8QuantParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(quant_clear_kernel, dim3((unsigned)((heads + 255) / 256)), dim3(256), 0, stream, amax,
                      (int)heads);
   const long code_rows = heads * (p.transposed ? n128 : p.n);
+  if (code_rows > 0x7fffffffL * 16) return hipErrorInvalidValue;
   switch (p.d) {
     case 64:
-      hipLaunchKernelGGL((quant_amax_kernel<64>), dim3((unsigned)(heads * chunks)), dim3(256), 0, stream,
+      hipLaunchKernelGGL((quant_amax_kernel<64>), dim3((unsigned)(heads * chunks)), dim3(kAmaxWaves * 64), 0, stream,
                          (const __bf16*)p.x, p.signs, amax, p.n, chunks);
-      hipLaunchKernelGGL((quant_codes_kernel<64>), dim3((unsigned)((code_rows + 3) / 4)), dim3(256), 0, stream,
-                         (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, heads, p.transposed);
+      if (p.transposed)
+        hipLaunchKernelGGL((quant_codes_t_kernel<64>), dim3((unsigned)(heads * (n128 / 64))), dim3(256), 0, stream,
+                           (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, n128 / 64);
+      else
+        hipLaunchKernelGGL((quant_codes_rows_kernel<64>), dim3((unsigned)((code_rows + 31) / 32)), dim3(256), 0,
+                           stream, (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, code_rows);
       break;
     case 128:
-      hipLaunchKernelGGL((quant_amax_kernel<128>), dim3((unsigned)(heads * chunks)), dim3(256), 0, stream,
+      hipLaunchKernelGGL((quant_amax_kernel<128>), dim3((unsigned)(heads * chunks)), dim3(kAmaxWaves * 64), 0, stream,
                          (const __bf16*)p.x, p.signs, amax, p.n, chunks);
-      hipLaunchKernelGGL((quant_codes_kernel<128>), dim3((unsigned)((code_rows + 3) / 4)), dim3(256), 0, stream,
-                         (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, heads, p.transposed);
+      if (p.transposed)
+        hipLaunchKernelGGL((quant_codes_t_kernel<128>), dim3((unsigned)(heads * (n128 / 64))), dim3(256), 0, stream,
+                           (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, n128 / 64);
+      else
+        hipLaunchKernelGGL((quant_codes_rows_kernel<128>), dim3((unsigned)((code_rows + 15) / 16)), dim3(256), 0,
+                           stream, (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, code_rows);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -111,6 +111,33 @@ def _counters(directory):
     return {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in res.items()}
 
 
+def overlap(cnt):
+    """Table of how a kernel's SIMD cycles split between the matrix cores and
+    the vector ALU, from the counters (kernels that have them all), or []."""
+    need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES",
+            "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+    rows = []
+    for k, cs in cnt.items():
+        if not all(c in cs for c in need) or not cs["GRBM_GUI_ACTIVE"] or not cs["SQ_VALU_MFMA_BUSY_CYCLES"]:
+            continue
+        simd = 1024 * cs["GRBM_GUI_ACTIVE"] / 8  # SIMD cycles of the launch
+        mfma = 100 * cs["SQ_VALU_MFMA_BUSY_CYCLES"] / simd
+        valu = 100 * 4 * cs["SQ_ACTIVE_INST_VALU"] / simd
+        co = 100 * cs["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd
+        wait = 100 * cs["SQ_WAIT_ANY"] / cs["SQ_WAVE_CYCLES"] if cs["SQ_WAVE_CYCLES"] else 0.0
+        fifo = cs.get("SQ_LDS_DATA_FIFO_FULL")
+        rows.append(f"| {k} | {mfma:.1f} | {valu:.1f} | {co:.1f} | {mfma + valu - co:.1f} | {wait:.1f} | "
+                    + (f"{fifo:.3g} |" if fifo is not None else "- |"))
+    if not rows:
+        return []
+    return ["Matrix cores and vector ALU (per SIMD cycle of the launch):", "",
+            "| kernel | MFMA busy % | VALU issue % | both at once % | either % | waves waiting % | "
+            "LDS data FIFO full |", "|---|---|---|---|---|---|---|"] + rows + [
+            "", "VALU issue % = 4 x SQ_ACTIVE_INST_VALU (a wave64 vector instruction occupies the 16-lane SIMD "
+            "for 4 cycles) / SIMD cycles; both at once % = SQ_VALU_MFMA_COEXEC_CYCLES / SIMD cycles; either % "
+            "= MFMA + VALU - both; waves waiting % = SQ_WAIT_ANY / SQ_WAVE_CYCLES."]
+
+
 def algorithmic_bytes(wl, kernel):
     """(read, write) bytes a kernel must move at least, per launch."""
     eb = 2 if wl.dtype == "bf16" else 4
@@ -168,7 +195,11 @@ def traffic(directory, workload_name, copy_mib, cmds):
                             "sources": [os.path.basename(f) for f in kernel_sources(k)],
                             "source_sha256": kernel_source_sha256(k)}
     out += ["", "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE/8 XCDs); clock = "
-            "(GRBM_GUI_ACTIVE/8) / trace duration; executed MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", "",
+            "(GRBM_GUI_ACTIVE/8) / trace duration; executed MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", ""]
+    ov = overlap(cnt)
+    if ov:
+        out += ov + [""]
+    out += [
             "Machine-readable (read by bench.py; a kernel's entry is valid only while the file that defines it and "
             "the shared headers, listed in `sources`, still hash to its `source_sha256`):",
             "", "```json", json.dumps(js, indent=1), "```"]

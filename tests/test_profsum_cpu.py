@@ -69,3 +69,15 @@ def test_paired_kernels_are_named_like_the_others():
     c5 = bench.kernel_names(workload("bf16_b2h8_n16384_d256_w512"))
     assert c5[0] == "fwd_pair_kernel<256,window>" and c5[2] == "bwd_kv_pair_kernel<256,window>"
     assert c5[3] == "bwd_q_pair_kernel<256,window>"
+
+
+def test_overlap_table_splits_simd_cycles():
+    # 8 XCDs x 1000 cycles -> 1024 SIMDs x 1000 SIMD cycles
+    cs = {"GRBM_GUI_ACTIVE": 8000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 512000.0, "SQ_ACTIVE_INST_VALU": 51200.0,
+          "SQ_VALU_MFMA_COEXEC_CYCLES": 102400.0, "SQ_WAIT_ANY": 30.0, "SQ_WAVE_CYCLES": 100.0,
+          "SQ_LDS_DATA_FIFO_FULL": 7.0}
+    rows = profsum.overlap({"k<128>": cs, "other": {"GRBM_GUI_ACTIVE": 1.0}})
+    row = [r for r in rows if r.startswith("| k<128>")]
+    # MFMA 50 %, VALU 4 x 5 % = 20 %, both 10 %, either 60 %, waiting 30 %
+    assert row == ["| k<128> | 50.0 | 20.0 | 10.0 | 60.0 | 30.0 | 7 |"]
+    assert profsum.overlap({"other": {"GRBM_GUI_ACTIVE": 1.0}}) == []
