@@ -159,37 +159,47 @@ def test_repeated_backward_is_bit_exact_over_many_workgroups(d, window):
 
 
 @pytest.mark.parametrize("n", [2048, 1990])
-def test_dense_d256_two_wave_kernel_matches_oracle_and_one_wave_kernel(n):
-    """d=256 without a window runs a two-waves-per-SIMD forward when the grid
-    holds at least two workgroups per CU (here 512 workgroups; n=1990 leaves
-    a ragged last tile), else the one-wave kernel.  The whole problem through
-    both (window = n selects the one-wave kernel with every key visible)
-    agrees to bf16 rounding, and two heads match the oracle."""
+def test_dense_d256_paired_kernels_on_a_large_grid(n):
+    """d=256 runs every pass on the paired-wave kernels.  On a grid of 512
+    workgroups (n=1990 leaves a ragged last tile) the all-keys kernels agree
+    with the window kernels given a window of n (every key visible) to bf16
+    rounding, repeat bit for bit, and two heads match the oracle."""
     import torch
     import exact_attention_69_amd as ea
-    from helpers import BF16_LSE_MAX_REL, BF16_O_MAX_REL, to_device
+    from helpers import BF16_GRAD_FRO_REL, BF16_LSE_MAX_REL, BF16_O_MAX_REL, fro_rel, to_device
     B, H, d = 2, 16, 256
     wl = make_case(B, H, n, d, "bf16", q_mult=3.0, seed=47)
-    print(f"[parity] two-wave d=256 forward {wl.name}", flush=True)
-    x = draw_inputs(wl, ("q", "k", "v"))
+    print(f"[parity] paired d=256 forward and backward {wl.name}", flush=True)
+    x = draw_inputs(wl)
     t = to_device(x, "bf16")
     o2, l2 = ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale)
-    for _ in range(10):  # repeats are bit-exact
+    g2 = ea.attn_bwd(t["q"], t["k"], t["v"], o2, t["do"], l2, wl.scale)
+    for _ in range(5):  # repeats are bit-exact
         o3, l3 = ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale)
+        g3 = ea.attn_bwd(t["q"], t["k"], t["v"], o2, t["do"], l2, wl.scale)
         torch.cuda.synchronize()
         assert torch.equal(o2, o3) and torch.equal(l2, l3)
+        assert all(torch.equal(a, b) for a, b in zip(g2, g3))
     o1, l1 = ea.attn_fwd(t["q"], t["k"], t["v"], wl.scale, window=n)
+    g1 = ea.attn_bwd(t["q"], t["k"], t["v"], o2, t["do"], l2, wl.scale, window=n)
     torch.cuda.synchronize()
     assert float((o2.float() - o1.float()).abs().max()) <= 1e-2 * float(o1.float().abs().max())
     assert float((l2 - l1).abs().max()) <= 1e-5 * float(l1.abs().max())
+    for a, b in zip(g2, g1):
+        assert fro_rel(a.float().cpu().numpy(), b.float().cpu().numpy()) <= 1e-2
     import oracle
     for h in (0, B * H - 1):
         sel = lambda a: a.reshape(B * H, n, d)[h][None, None]
-        O, L = oracle.attention_forward(sel(x["q"]), sel(x["k"]), sel(x["v"]), wl.scale)
+        q, k, v, do = (sel(x[key]) for key in ("q", "k", "v", "do"))
+        O, L = oracle.attention_forward(q, k, v, wl.scale)
+        dQ, dK, dV = oracle.attention_backward(q, k, v, do, wl.scale)
         og = o2.reshape(B * H, n, d)[h].float().cpu().numpy()
         lg = l2.reshape(B * H, n)[h].cpu().numpy()
         assert np.max(np.abs(og - O[0, 0])) <= BF16_O_MAX_REL * np.max(np.abs(O))
         assert np.max(np.abs(lg - L[0, 0])) <= BF16_LSE_MAX_REL * np.max(np.abs(L))
+        for got, ref in zip(g2, (dQ, dK, dV)):
+            gh = got.reshape(B * H, n, d)[h].float().cpu().numpy()
+            assert fro_rel(gh, ref[0, 0]) <= BF16_GRAD_FRO_REL
 
 
 def test_backward_is_deterministic():
