@@ -56,6 +56,13 @@ BF16_CASES = [
     (1, 1, 700, 128, 70, 1.0),    # window spanning a few tiles
     (1, 1, 600, 256, 100, 1.0),
     (1, 1, 513, 64, 200, 1.0),
+    # the paired-wave kernels at d=256: a single row, one partial tile, a
+    # ragged multi-head grid with peaky rows, windows narrower than a tile
+    (1, 1, 1, 256, -1, 1.0),
+    (1, 1, 33, 256, -1, 1.0),
+    (2, 3, 257, 256, -1, 3.0),
+    (1, 2, 300, 256, 0, 1.0),
+    (1, 1, 333, 256, 3, 1.0),
 ]
 
 
@@ -64,10 +71,11 @@ def test_bf16_parity(B, H, n, d, window, q_mult):
     _run(B, H, n, d, "bf16", window, q_mult)
 
 
-def test_window_zero_identities_bf16():
+@pytest.mark.parametrize("d", [64, 256])
+def test_window_zero_identities_bf16(d):
     # window = 0: each row sees only its own key, so O = V exactly (bf16 in,
     # bf16 out), LSE = scale q.k, and dQ = dK = 0, dV = dO.
-    wl = make_case(1, 1, 130, 64, "bf16", 0)
+    wl = make_case(1, 1, 130, d, "bf16", 0)
     inputs = draw_inputs(wl)
     got = run_gpu(wl, inputs)
     np.testing.assert_array_equal(got["o"], inputs["v"])
