@@ -473,34 +473,37 @@ __global__ __launch_bounds__(kF8NW * 64, 2) void fwd_fp8_kernel(
 int fp8_padded_n(int n) { return (n + kF8BC - 1) / kF8BC * kF8BC; }
 
 hipError_t launch_quant_fp8(const Fp8QuantParams& p, hipStream_t stream) {
+  if (p.d != 64 && p.d != 128) return hipErrorInvalidValue;
   const long heads = (long)p.B * p.H;
   const int chunks = (p.n + kAmaxRows - 1) / kAmaxRows;  // amax workgroups per head
-  if (heads * chunks > 0x7fffffffL) return hipErrorInvalidValue;
   const int n128 = fp8_padded_n(p.n);
+  const long code_rows = heads * (p.transposed ? n128 : p.n);
+  // every grid (amax; codes: a 64-key group or 256 / (d/8) rows per
+  // workgroup) checked before the first launch
+  const long code_blocks = p.transposed ? heads * (n128 / 64) : (code_rows + 256 / (p.d / 8) - 1) / (256 / (p.d / 8));
+  if (heads * chunks > 0x7fffffffL || code_blocks > 0x7fffffffL || heads > 0x7fffffffL) return hipErrorInvalidValue;
   uint32_t* amax = (uint32_t*)p.scale;
   hipLaunchKernelGGL(quant_clear_kernel, dim3((unsigned)((heads + 255) / 256)), dim3(256), 0, stream, amax,
                      (int)heads);
-  const long code_rows = heads * (p.transposed ? n128 : p.n);
-  if (code_rows > 0x7fffffffL * 16) return hipErrorInvalidValue;
   switch (p.d) {
     case 64:
       hipLaunchKernelGGL((quant_amax_kernel<64>), dim3((unsigned)(heads * chunks)), dim3(kAmaxWaves * 64), 0, stream,
                          (const __bf16*)p.x, p.signs, amax, p.n, chunks);
       if (p.transposed)
-        hipLaunchKernelGGL((quant_codes_t_kernel<64>), dim3((unsigned)(heads * (n128 / 64))), dim3(256), 0, stream,
+        hipLaunchKernelGGL((quant_codes_t_kernel<64>), dim3((unsigned)code_blocks), dim3(256), 0, stream,
                            (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, n128 / 64);
       else
-        hipLaunchKernelGGL((quant_codes_rows_kernel<64>), dim3((unsigned)((code_rows + 31) / 32)), dim3(256), 0,
+        hipLaunchKernelGGL((quant_codes_rows_kernel<64>), dim3((unsigned)code_blocks), dim3(256), 0,
                            stream, (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, code_rows);
       break;
     case 128:
       hipLaunchKernelGGL((quant_amax_kernel<128>), dim3((unsigned)(heads * chunks)), dim3(kAmaxWaves * 64), 0, stream,
                          (const __bf16*)p.x, p.signs, amax, p.n, chunks);
       if (p.transposed)
-        hipLaunchKernelGGL((quant_codes_t_kernel<128>), dim3((unsigned)(heads * (n128 / 64))), dim3(256), 0, stream,
+        hipLaunchKernelGGL((quant_codes_t_kernel<128>), dim3((unsigned)code_blocks), dim3(256), 0, stream,
                            (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, n128, n128 / 64);
       else
-        hipLaunchKernelGGL((quant_codes_rows_kernel<128>), dim3((unsigned)((code_rows + 15) / 16)), dim3(256), 0,
+        hipLaunchKernelGGL((quant_codes_rows_kernel<128>), dim3((unsigned)code_blocks), dim3(256), 0,
                            stream, (const __bf16*)p.x, p.signs, amax, (uint8_t*)p.x8, p.n, code_rows);
       break;
     default: return hipErrorInvalidValue;
