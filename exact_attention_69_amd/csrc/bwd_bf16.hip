@@ -577,6 +577,10 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
   // At d = 128: the barrier after the P-wave's S products (no memory is
   // handed over through it).
   constexpr bool kMidSync = D == 128;
+  // LDS reads issued this many fragments ahead of their products (at d = 128
+  // 4 rather than 2: 3% faster at n = 8192, 5% at n = 1000; 3, 6 and 8 were
+  // slower than 4)
+  constexpr int kPairLead = D == 128 ? 4 : 2;
   auto mid_sync = [&]() {
     if constexpr (kMidSync) {
       __builtin_amdgcn_sched_barrier(0);
@@ -664,7 +668,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(qf, kr[kb][ds], s[kb]);
         }
-        pair_sched_products<NDS, 1, 2, NKB>();
+        pair_sched_products<NDS, 1, kPairLead, NKB>();
         __builtin_amdgcn_sched_barrier(0);
       }
       mid_sync();
@@ -709,7 +713,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) acc[kb][db] = mfma32(a, pb[kb][half], acc[kb][db]);
           }
-        pair_sched_products<2 * NDB, 2, 2, NKB>();
+        pair_sched_products<2 * NDB, 2, kPairLead, NKB>();
       }
       end_iteration();
     }
@@ -760,7 +764,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) acc[kb][db] = mfma32(a, sb[kb][half], acc[kb][db]);
           }
-        pair_sched_products<2 * NDB, 2, 2, NKB>();
+        pair_sched_products<2 * NDB, 2, kPairLead, NKB>();
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i < steps && pair_sees(i)) {
@@ -787,7 +791,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_pair_kernel(
           dp[0] = mfma32(gf, v0[ds], dp[0]);
           if constexpr (NKB == 2) dp[1] = mfma32(gf, ld_row(0, vbase ^ (32 * ds)), dp[1]);
         }
-        pair_sched_products<NDS, NKB, 2, NKB>();
+        pair_sched_products<NDS, NKB, kPairLead, NKB>();
       }
       end_iteration();
     }
