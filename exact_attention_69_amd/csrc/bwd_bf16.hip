@@ -18,6 +18,11 @@
 //   3. query side (Q-outer): a workgroup owns 32*NW query rows and
 //      accumulates dQ over the key tiles, recomputing S and dP with lanes
 //      indexed by query row.
+//
+// The d = 128 instantiations without a mask are compiled in a translation
+// unit of their own (bwd_bf16_d128.hip includes this file with
+// EXATTN_BWD_D128 defined), which the build gives a different instruction
+// scheduler; this file's own unit holds the rest and the entry points.
 #include "bwd_common.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -1431,17 +1436,29 @@ hipError_t bwd_d(const BwdParams& p, unsigned stages, hipStream_t stream) {
   return hipSuccess;
 }
 
+#ifndef EXATTN_BWD_D128
 template <int MODE>
 hipError_t bwd_mode(const BwdParams& p, unsigned stages, hipStream_t stream) {
   switch (p.d) {
     case 64: return bwd_d<64, MODE>(p, stages, stream);
-    case 128: return bwd_d<128, MODE>(p, stages, stream);
+    case 128:
+      if constexpr (MODE == kMaskNone)
+        return launch_bwd_bf16_d128(p, stages, stream);
+      else
+        return bwd_d<128, MODE>(p, stages, stream);
     case 256: return bwd_d<256, MODE>(p, stages, stream);
     default: return hipErrorInvalidValue;
   }
 }
+#endif
 
 }  // namespace
+
+#ifdef EXATTN_BWD_D128
+hipError_t launch_bwd_bf16_d128(const BwdParams& p, unsigned stages, hipStream_t stream) {
+  return bwd_d<128, kMaskNone>(p, stages, stream);
+}
+#else
 
 hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stream) {
   if (p.pattern_kv.list != nullptr) {
@@ -1470,5 +1487,6 @@ void bwd_q_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* wa
   }
   *rows_per_block = 32 * *waves;
 }
+#endif
 
 }  // namespace exattn

@@ -58,6 +58,9 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 // Backward stages: rowdot (D), key side (dK, dV), query side (dQ).
 enum BwdStage : unsigned { kStageRowdot = 1, kStageKV = 2, kStageQ = 4, kStageAll = 7 };
 hipError_t launch_bwd_bf16(const BwdParams& p, unsigned stages, hipStream_t stream);
+// The part of launch_bwd_bf16 for d = 128 without a mask (a translation unit
+// of its own).
+hipError_t launch_bwd_bf16_d128(const BwdParams& p, unsigned stages, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdParams& p, unsigned stages, hipStream_t stream);
 
 // FP8: per-head quantiser (optional Hadamard rotation) and the forward.

@@ -24,8 +24,9 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
 def kernel_sources(kernel=None):
-    """Source files a kernel is built from: the file that defines it plus
-    every shared header (all sources when `kernel` is None or not found)."""
+    """Source files a kernel is built from: the file that defines it, the
+    units that include that file, and every shared header (all sources when
+    `kernel` is None or not found)."""
     files = sorted(glob.glob(os.path.join(CSRC, "*")))
     if kernel is None:
         return files
@@ -34,7 +35,10 @@ def kernel_sources(kernel=None):
     home = [f for f in files if pat.search(open(f, encoding="utf-8", errors="replace").read())]
     if not home:
         return files
-    return sorted(set(home) | {f for f in files if f.endswith(".hpp")})
+    # units that compile the home file under other settings (#include "home")
+    inc = {f for f in files for h in home
+           if f'#include "{os.path.basename(h)}"' in open(f, encoding="utf-8", errors="replace").read()}
+    return sorted(set(home) | inc | {f for f in files if f.endswith(".hpp")})
 
 
 def kernel_source_sha256(kernel=None):
