@@ -39,10 +39,12 @@ def common_flags():
     ]
 
 
-# Flags for single sources: the d = 128 backward kernels without a mask are
-# compiled with LLVM's max-ilp machine scheduler (faster there; slower with a
-# window and at d = 64 and 256).
-SOURCE_FLAGS = {"bwd_bf16_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Flags for single sources: some instantiations are compiled with LLVM's
+# max-ilp machine scheduler, where it measured faster (the d = 128 backward
+# without a mask; the d = 128 forward without a mask and the d = 256 forward
+# with a window); each unit's header gives the measurements.
+MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+SOURCE_FLAGS = {"bwd_bf16_d128.hip": MAX_ILP, "fwd_bf16_ilp.hip": MAX_ILP}
 
 
 def sources():

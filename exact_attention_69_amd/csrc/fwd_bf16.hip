@@ -27,6 +27,12 @@
 // the vector ALU exponentiates tile t the matrix cores already compute S for
 // tile t+1; the two instruction streams are interleaved explicitly.
 // Scores are handled in the base-2 domain: exp(scale*s) = 2^(scale*log2e*s).
+//
+// Two instantiations, d = 128 without a mask and d = 256 with a window, are
+// compiled in a translation unit of their own (fwd_bf16_ilp.hip includes this
+// file with EXATTN_FWD_ILP defined), which the build gives a different
+// instruction scheduler; this file's own unit holds the rest and the entry
+// points.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "pattern.hpp"
@@ -794,17 +800,35 @@ hipError_t launch_d_main(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#ifndef EXATTN_FWD_ILP
 template <int MODE>
 hipError_t launch_mode(const FwdParams& p, hipStream_t stream) {
   switch (p.d) {
     case 64: return launch_d<64, MODE>(p, stream);
-    case 128: return launch_d<128, MODE>(p, stream);
-    case 256: return launch_d<256, MODE>(p, stream);
+    case 128:
+      if constexpr (MODE == kMaskNone)
+        return launch_fwd_bf16_ilp(p, stream);
+      else
+        return launch_d<128, MODE>(p, stream);
+    case 256:
+      if constexpr (MODE == kMaskWindow)
+        return launch_fwd_bf16_ilp(p, stream);
+      else
+        return launch_d<256, MODE>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
+#endif
 
 }  // namespace
+
+#ifdef EXATTN_FWD_ILP
+hipError_t launch_fwd_bf16_ilp(const FwdParams& p, hipStream_t stream) {
+  if (p.d == 128 && p.window < 0) return launch_d<128, kMaskNone>(p, stream);
+  if (p.d == 256 && p.window >= 0) return launch_d<256, kMaskWindow>(p, stream);
+  return hipErrorInvalidValue;
+}
+#else
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   if (p.pattern.list != nullptr) {
@@ -829,5 +853,6 @@ void fwd_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* wave
   }
   *rows_per_block = 32 * *waves;
 }
+#endif
 
 }  // namespace exattn

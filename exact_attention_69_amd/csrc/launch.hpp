@@ -50,6 +50,9 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+// The part of launch_fwd_bf16 for d = 128 without a mask and d = 256 with a
+// window, without a pattern (a translation unit of its own).
+hipError_t launch_fwd_bf16_ilp(const FwdParams& p, hipStream_t stream);
 // Workgroup geometry of the bf16 kernels in pattern mode, for the pattern plan.
 void fwd_bf16_geometry(int d, int* rows_per_block, int* keys_per_tile, int* waves);
 void bwd_kv_bf16_geometry(int d, int* keys_per_block, int* rows_per_tile, int* waves);
