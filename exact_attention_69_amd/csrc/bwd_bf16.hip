@@ -431,19 +431,22 @@ __device__ __forceinline__ void pair_sched_products() {
 // second in LDS, which leaves registers for the dP it carries over.  At
 // d = 256 this splits the 512 accumulator registers a single wave would need
 // for 32 keys (dK and dV, 2 x 256 columns) over the two waves, so two waves
-// per SIMD fit where one did.  The dS-wave's instructions win the SIMD's
-// issue arbitration: its chain of short phases is the one that stalls on LDS
-// reads.  At d = 128 the waves also meet at a second barrier once the P-wave
-// has issued S(i), and the priority follows the products: the P-wave's while
-// it forms S, the dS-wave's from that barrier on.  Left alone, the dS-wave's
-// dK products took the matrix cores while S was still waiting for them, and
-// the P-wave's exponentials started late (phase timestamps per wave); with the
-// barrier the pass is 1.5% faster there (at d = 256 it was 9% slower).
+// per SIMD fit where one did.  At d = 256 the dS-wave's instructions win the
+// SIMD's issue arbitration throughout: its chain of short phases is the one
+// that stalls on LDS reads.  At d = 128 the waves also meet at a second
+// barrier once the P-wave has issued S(i), and the priority follows the
+// products: the P-wave's while it forms S, the dS-wave's from that barrier
+// on.  Left alone, the dS-wave's dK products took the matrix cores while S
+// was still waiting for them, and the P-wave's exponentials started late
+// (phase timestamps per wave); with the barrier the pass is 1.5% faster there
+// (at d = 256 it was 9% slower).  Also at d = 128, the LDS reads run four
+// fragments ahead of their products and the P-wave issues its share of the
+// next tile's copies after S (see kPairLead and load_tile's call sites).
 // Buffers: three Q/dO tiles (tiles i-1 and i are read while i+1 is in
-// flight) and two P tiles.  LDS read addresses are
-// per-lane bases (the tile buffer's offset added once per iteration) XOR a
-// constant, plus a constant offset: four base registers instead of one per
-// fragment, because every register is taken.
+// flight) and two P tiles.  LDS read addresses are per-lane bases (the tile
+// buffer's offset added once per iteration) XOR a constant, plus a constant
+// offset: four base registers instead of one per fragment, because every
+// register is taken.
 template <int D>
 struct PairKv {
   static constexpr int NKB = D == 128 ? 2 : 1;  // 32-key blocks per pair
