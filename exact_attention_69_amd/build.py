@@ -57,7 +57,8 @@ def sources():
 
 def _compile(src, verbose, build_dir=BUILD, extra=()):
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + SOURCE_FLAGS.get(os.path.basename(src), []) + list(extra) + ["-c", src, "-o", obj]
+    unit_flags = SOURCE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc()] + common_flags() + unit_flags + list(extra) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -132,7 +133,8 @@ def build_sanitized(verbose=False):
             objs.append(obj)
         else:
             obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-            newest = max(os.path.getmtime(os.path.join(CSRC, f)) for f in os.listdir(CSRC))  # sources include each other
+            # sources include each other: rebuild when any of them is newer
+            newest = max(os.path.getmtime(os.path.join(CSRC, f)) for f in os.listdir(CSRC))
             if not os.path.exists(obj) or os.path.getmtime(obj) < newest:
                 obj = _compile(src, verbose)
             objs.append(obj)

@@ -493,8 +493,14 @@ int attn_bwd_pattern(int dtype, int B, int H, int n, int d, const void* Q, const
   if (workspace_bytes < L.total) return EXATTN_EWORKSPACE;
   const size_t tb = (size_t)B * H * n * d * elem_bytes(dtype);
   const size_t lb = (size_t)B * H * n * sizeof(float);
-  const Span ins[] = {{Q, tb}, {K, tb}, {V, tb}, {O, tb}, {dO, tb}, {LSE, lb},
-                      {pattern->global_idx, (size_t)pattern->n_global * 4}, {pattern->layout, layout_bytes(pattern, n)}};
+  const Span ins[] = {{Q, tb},
+                      {K, tb},
+                      {V, tb},
+                      {O, tb},
+                      {dO, tb},
+                      {LSE, lb},
+                      {pattern->global_idx, (size_t)pattern->n_global * 4},
+                      {pattern->layout, layout_bytes(pattern, n)}};
   const Span outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {workspace, L.total}};
   for (int o = 0; o < 4; ++o) {
     for (const Span& in : ins)
