@@ -137,13 +137,15 @@ def kernel_names(wl):
     return [f"{fwd}<{d}{m}>", f"bwd_rowdot_kernel<{d}>", f"{kv}<{d}{m}>", f"{dq}<{d}{m}>"]
 
 
-def time_steps(wl, steps, warmup, graph=False):
+def time_steps(wl, steps, warmup, graph=False, one_call=False):
     """Run `warmup` untimed and `steps` timed steps of the workload with its
     inputs resident on the GPU; returns (names and average ms of the calls of
     a step, ms per step, wall seconds of the timed region).  Dense workloads
     time the four kernels of a step (forward, rowdot, dK/dV, dQ) one call
-    each; sparse-pattern workloads time attn_fwd_pattern and attn_bwd_pattern
-    (each including its plan kernels).  With graph=True the step's calls are
+    each, or with one_call=True the forward and the whole backward as one
+    attn_bwd call (which, with a window, runs its dK/dV and dQ kernels side
+    by side on two streams); sparse-pattern workloads time attn_fwd_pattern
+    and attn_bwd_pattern (each including its plan kernels).  With graph=True the step's calls are
     captured once in a HIP graph and the graph is replayed instead (the same
     kernels, without the host's per-call overhead); only the whole steps are
     timed then."""
@@ -201,6 +203,12 @@ def time_steps(wl, steps, warmup, graph=False):
                  lambda: ea.attn_bwd_rowdot(o, do, lse, workspace=ws, stream=None),
                  lambda: attn_bwd_dkdv(q, k, v, do, lse, ws, wl.scale, wl.window, dk=dk, dv=dv, stream=None),
                  lambda: attn_bwd_dq(q, k, v, do, lse, ws, wl.scale, wl.window, dq=dq, stream=None))
+        if one_call:
+            attn_bwd = ea.attn_bwd_gqa if gqa else ea.attn_bwd
+            names = ["attn_fwd", "attn_bwd"]
+            calls = (calls[0],
+                     lambda: attn_bwd(q, k, v, o, do, lse, wl.scale, wl.window, workspace=ws, dq=dq, dk=dk, dv=dv,
+                                      stream=None))
     for _ in range(warmup):
         for c in calls:
             c()
@@ -385,6 +393,12 @@ def main(argv=None):
             _, _, gms, _ = time_steps(cw, 5 if cw.n >= 32768 else 20, 2, graph=True)
             configs[cw.name]["step_ms_graph_median"] = round(gms, 4)
             configs[cw.name]["tflops_graph"] = round((cf + cb) / (gms * 1e-3) / 1e12, 2)
+            if not cw.has_pattern and not cw.fp8:
+                # the step as a caller runs it: attn_fwd, then one attn_bwd call
+                time_steps(cw, 5 if cw.n >= 32768 else 20, 2, one_call=True)
+                oms = statistics.median(time_steps.last_step_ms)
+                configs[cw.name]["step_ms_one_call_median"] = round(oms, 4)
+                configs[cw.name]["tflops_one_call"] = round((cf + cb) / (oms * 1e-3) / 1e12, 2)
 
     if args.copy_calibration:
         import torch

@@ -134,8 +134,77 @@ exattn::BwdParams bwd_params(const void* Q, const void* K, const void* V, const 
   return exattn::BwdParams{Q, K, V, O, dO, LSE, dQ, dK, dV, ws, lse2, B, H, n, d, scale, window, group};
 }
 
-int run_bwd(int dtype, const exattn::BwdParams& p, unsigned stages, void* stream) {
+// A second stream per device for the key-side pass of a windowed backward.
+// With a window each pass has few key tiles per block and leaves part of the
+// GPU idle at its tail; once the row statistics exist the two passes are
+// independent, so running them side by side fills those gaps (3-8% faster in
+// measurement).  Without a window they compete for the same matrix cores and
+// the overlap measured slower, so dense and pattern problems stay on one
+// stream; so does a call under graph capture.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;  // held from the fork to the join of one call
+SideStream g_side[kMaxSideDevices];
+
+// The side stream of the device `s` runs on, created on first use (default
+// priority, non-blocking); nullptr when it is unavailable.
+SideStream* side_stream_for(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  if (s != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  }
+  SideStream& g = g_side[dev];
+  if (g.stream == nullptr) {
+    hipStream_t t = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipStreamCreateWithFlags(&t, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+      if (a != nullptr) (void)hipEventDestroy(a);
+      (void)hipStreamDestroy(t);
+      return nullptr;
+    }
+    g.fork = a;
+    g.join = b;
+    g.stream = t;
+  }
+  return &g;
+}
+
+bool split_backward(int dtype, const exattn::BwdParams& p, unsigned stages, hipStream_t s) {
+  if (dtype != EXATTN_BF16 || stages != exattn::kStageAll || p.window < 0 || p.pattern_kv.list != nullptr)
+    return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
+}
+
+// `may_split`: the call may put the key-side pass on the device's side stream
+// (the allocation-free entry point passes false: it creates nothing).
+int run_bwd(int dtype, const exattn::BwdParams& p, unsigned stages, void* stream, bool may_split = false) {
   hipStream_t s = (hipStream_t)stream;
+  if (may_split && split_backward(dtype, p, stages, s)) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if (SideStream* side = side_stream_for(s)) {
+      hipError_t e = exattn::launch_bwd_bf16(p, exattn::kStageRowdot, s);
+      if (e != hipSuccess) return from_hip(e);
+      e = hipEventRecord(side->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+      if (e != hipSuccess) return from_hip(e);
+      // from here the side stream waits on `s`; it is joined back whatever
+      // the launches return, so nothing the call started outlives its stream
+      hipError_t eq = exattn::launch_bwd_bf16(p, exattn::kStageQ, s);
+      hipError_t ekv = eq == hipSuccess ? exattn::launch_bwd_bf16(p, exattn::kStageKV, side->stream) : hipSuccess;
+      e = hipEventRecord(side->join, side->stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+      return from_hip(eq != hipSuccess ? eq : ekv != hipSuccess ? ekv : e);
+    }
+  }
   hipError_t e = dtype == EXATTN_BF16 ? exattn::launch_bwd_bf16(p, stages, s) : exattn::launch_bwd_f32(p, stages, s);
   return from_hip(e);
 }
@@ -158,7 +227,7 @@ int attn_bwd_gqa(int dtype, int B, int H, int Hkv, int n, int d, const void* Q, 
   st = check_bwd(dtype, B, H, Hkv, n, d, scale, window, ins, 6, outs, 4, workspace_bytes);
   if (st != EXATTN_OK) return st;
   return run_bwd(dtype, bwd_params(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, n, d, scale, window, H / Hkv),
-                 exattn::kStageAll, stream);
+                 exattn::kStageAll, stream, true);
 }
 
 int attn_bwd(int dtype, int B, int H, int n, int d, const void* Q, const void* K, const void* V,

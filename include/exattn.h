@@ -138,7 +138,12 @@ size_t attn_bwd_workspace_bytes(int dtype, int B, int H, int n, int d);
  *   workspace, workspace_bytes : caller-owned device scratch, at least
  *             attn_bwd_workspace_bytes(); its contents on entry are ignored
  *             and on return are unspecified.
- *   stream  : hipStream_t to enqueue on.
+ *   stream  : hipStream_t to enqueue on.  With a window (bf16, outside
+ *             graph capture) the dK/dV stage runs on a second stream of the
+ *             same device that the library creates on first use (default
+ *             priority); it is forked from `stream` after the rowdot stage
+ *             and joined back before the call returns, so all of the call's
+ *             work is ordered on `stream` as if it ran there alone.
  * Returns an exattn_status.
  */
 int attn_bwd(int dtype, int B, int H, int n, int d,
@@ -151,7 +156,8 @@ int attn_bwd(int dtype, int B, int H, int n, int d,
 
 /*
  * The backward as three stages, each exactly one kernel launch; attn_bwd is
- * these three in order on one stream.  Stage 1 must complete before stages
+ * these three (rowdot, then dK/dV and dQ on two streams with a window, else
+ * in order on one stream).  Stage 1 must complete before stages
  * 2 and 3 (stream order does it); stages 2 and 3 are independent of each
  * other (they may run on two streams once stage 1 is done) and either may
  * be skipped when its gradients are not wanted.  Arguments mean what they
@@ -197,7 +203,8 @@ int attn_bwd_dq(int dtype, int B, int H, int n, int d,
  * attn_bwd, minus the workspace: the rowdot stage's two fp32 row arrays go
  * to a fixed device buffer of EXATTN_NOALLOC_SCRATCH_BYTES (16 MiB) that the
  * library holds on each GPU it runs on until the process ends.  The call
- * makes no hipMalloc/hipFree and no allocating library call.  Problems whose
+ * makes no hipMalloc/hipFree and no allocating library call, and enqueues
+ * everything on `stream` (no second stream, with or without a window).  Problems whose
  * attn_bwd_workspace_bytes() exceeds the buffer (B*H*n > 2^21 rows) return
  * EXATTN_ESCRATCH with nothing launched.  All calls on one GPU share its
  * buffer: two calls that may overlap on one GPU (different streams, or

@@ -262,6 +262,45 @@ def test_staged_backward_matches_attn_bwd(dtype, window):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d,Hkv", [(64, 2), (128, 4), (256, 1)])
+def test_windowed_backward_on_two_streams_stays_ordered_on_its_stream(d, Hkv):
+    """With a window, attn_bwd puts its dK/dV stage on a second stream forked
+    from the call's stream after the rowdot stage and joined back before it
+    returns.  Two calls in a row on a stream that is not the current one write
+    into the same gradient tensors; copies taken on that stream right after
+    each call, with no host synchronisation, must equal the one-stream staged
+    backward (rowdot, dK/dV, dQ in order) bit for bit."""
+    import torch
+    import exact_attention_69_amd as ea
+    B, H, n, w = 2, 4, 1500, 100
+    print(f"[parity] two-stream backward d={d} Hkv={Hkv} n={n} window={w}", flush=True)
+    cur = torch.cuda.current_stream()
+    s = torch.cuda.Stream()
+    dq = torch.empty(B, H, n, d, dtype=torch.bfloat16, device="cuda")
+    dk = torch.empty(B, Hkv, n, d, dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    got, want, keep = [], [], []
+    for seed in (5, 6):
+        g = torch.Generator().manual_seed(seed)
+        q, do = (torch.randn(B, H, n, d, generator=g).bfloat16().cuda() for _ in range(2))
+        k, v = (torch.randn(B, Hkv, n, d, generator=g).bfloat16().cuda() for _ in range(2))
+        s.wait_stream(cur)
+        o, lse = ea.attn_fwd_gqa(q, k, v, window=w, stream=s)
+        ea.attn_bwd_gqa(q, k, v, o, do, lse, window=w, dq=dq, dk=dk, dv=dv, stream=s)
+        with torch.cuda.stream(s):
+            got.append(tuple(x.clone() for x in (dq, dk, dv)))
+        ws = ea.attn_bwd_rowdot(o, do, lse, stream=s)
+        rk, rv = ea.attn_bwd_dkdv_gqa(q, k, v, do, lse, ws, window=w, stream=s)
+        rq = ea.attn_bwd_dq_gqa(q, k, v, do, lse, ws, window=w, stream=s)
+        want.append((rq, rk, rv))
+        keep.append((q, k, v, do, o, lse, ws))
+    torch.cuda.synchronize()
+    for a, b in zip(got, want):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+    assert not torch.equal(got[0][0], got[1][0])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rowdot_workspace_holds_negated_d_and_base2_lse(dtype):
     """attn_bwd_rowdot's workspace: -D = -rowsum(dO * O) in the first region
