@@ -301,6 +301,54 @@ def test_windowed_backward_on_two_streams_stays_ordered_on_its_stream(d, Hkv):
     assert not torch.equal(got[0][0], got[1][0])
 
 
+def test_windowed_backward_from_two_threads():
+    """Two host threads, each with its own stream and inputs, call the
+    windowed attn_bwd (whose dK/dV stage goes to the device's shared second
+    stream) six times each at the same time.  Every call's gradients must
+    equal that thread's one-stream staged backward bit for bit."""
+    import threading
+    import torch
+    import exact_attention_69_amd as ea
+    B, H, n, d, w = 1, 4, 700, 128, 64
+    print(f"[parity] two-thread windowed backward n={n} d={d} window={w}", flush=True)
+    cur = torch.cuda.current_stream()
+    jobs = []
+    for seed in (11, 12):
+        g = torch.Generator().manual_seed(seed)
+        q, k, v, do = (torch.randn(B, H, n, d, generator=g).bfloat16().cuda() for _ in range(4))
+        o, lse = ea.attn_fwd(q, k, v, window=w)
+        ws = ea.attn_bwd_rowdot(o, do, lse)
+        rk, rv = ea.attn_bwd_dkdv(q, k, v, do, lse, ws, window=w)
+        rq = ea.attn_bwd_dq(q, k, v, do, lse, ws, window=w)
+        jobs.append(dict(args=(q, k, v, o, do, lse), ref=(rq, rk, rv), stream=torch.cuda.Stream(), got=[]))
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(job):
+        try:
+            s = job["stream"]
+            s.wait_stream(cur)
+            with torch.cuda.stream(s):
+                for _ in range(6):
+                    out = ea.attn_bwd(*job["args"], window=w, stream=s)
+                    job["got"].append(tuple(x.clone() for x in out))
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for job in jobs:
+        assert len(job["got"]) == 6
+        for got in job["got"]:
+            for x, y in zip(got, job["ref"]):
+                assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rowdot_workspace_holds_negated_d_and_base2_lse(dtype):
     """attn_bwd_rowdot's workspace: -D = -rowsum(dO * O) in the first region
