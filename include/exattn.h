@@ -51,13 +51,17 @@
  *   Supported head dims d: 64, 128, 256.  Any n >= 1 (ragged tails masked).
  *
  * Ownership and execution
- *   The caller allocates and owns every buffer; the library allocates nothing
- *   and keeps no pointer after a call returns.  Inputs are read only; outputs
- *   are completely overwritten (no need to clear them).  Every call only
- *   enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *   The caller allocates and owns every buffer; the library allocates no
+ *   device memory besides the fixed buffer of attn_bwd_noalloc, and keeps no
+ *   pointer after a call returns.  Inputs are read only; outputs are
+ *   completely overwritten (no need to clear them).  Every call only
+ *   enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
  *   returns without synchronising; a device fault surfaces at the caller's
- *   next synchronisation.  Calls are reentrant; two calls that share an
- *   output or workspace buffer must be ordered by the caller.
+ *   next synchronisation.  (The one exception, attn_bwd with a window, also
+ *   uses a second stream of the device that it forks from `stream` and
+ *   joins back before returning; see attn_bwd.)  Calls are reentrant; two
+ *   calls that share an output or workspace buffer must be ordered by the
+ *   caller.
  *
  * Errors (no exception crosses the ABI; nothing is launched on error)
  *   EXATTN_EINVAL       null pointer, B/H/n < 1, Hkv < 1 or not dividing H,
