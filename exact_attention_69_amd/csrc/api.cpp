@@ -137,7 +137,7 @@ exattn::BwdParams bwd_params(const void* Q, const void* K, const void* V, const 
 // A second stream per device for the key-side pass of a windowed backward.
 // With a window each pass has few key tiles per block and leaves part of the
 // GPU idle at its tail; once the row statistics exist the two passes are
-// independent, so running them side by side fills those gaps (3-8% faster in
+// independent, so running them side by side fills those gaps (3-9% faster in
 // measurement).  Without a window they compete for the same matrix cores and
 // the overlap measured slower, so dense and pattern problems stay on one
 // stream; so does a call under graph capture.
