@@ -393,11 +393,20 @@ def main(argv=None):
             _, _, gms, _ = time_steps(cw, 5 if cw.n >= 32768 else 20, 2, graph=True)
             configs[cw.name]["step_ms_graph_median"] = round(gms, 4)
             configs[cw.name]["tflops_graph"] = round((cf + cb) / (gms * 1e-3) / 1e12, 2)
-            if not cw.has_pattern and not cw.fp8:
-                # the step as a caller runs it: attn_fwd, then one attn_bwd call
-                time_steps(cw, 5 if cw.n >= 32768 else 20, 2, one_call=True)
-                oms = statistics.median(time_steps.last_step_ms)
+            if cw.window >= 0 and not cw.has_pattern and not cw.fp8:
+                # With a window a single attn_bwd call runs its two gradient
+                # passes on two streams: the step as a caller runs it
+                # (attn_fwd, then one attn_bwd call), timed in turns with the
+                # stage calls above so that both see the same clock.
+                one, staged = [], []
+                for _ in range(2):
+                    time_steps(cw, 10, 2, one_call=True)
+                    one += time_steps.last_step_ms
+                    time_steps(cw, 10, 2)
+                    staged += time_steps.last_step_ms
+                oms = statistics.median(one)
                 configs[cw.name]["step_ms_one_call_median"] = round(oms, 4)
+                configs[cw.name]["step_ms_stage_calls_alternating_median"] = round(statistics.median(staged), 4)
                 configs[cw.name]["tflops_one_call"] = round((cf + cb) / (oms * 1e-3) / 1e12, 2)
 
     if args.copy_calibration:
