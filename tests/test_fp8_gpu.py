@@ -8,7 +8,6 @@ fp64 attention of the oracle's own codes; the difference is the GPU's
 rounding of P to E4M3 before the P V product, bounded below.
 """
 
-import math
 import sys
 
 import numpy as np
