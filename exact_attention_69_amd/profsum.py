@@ -281,7 +281,11 @@ def sparse_io(directory, names, copy_mib, lds_kib, cmds):
 
 
 if __name__ == "__main__":
-    mode = sys.argv[1]
+    nargs = {"stats": 2, "pmc": 2, "traffic": 4, "sparseio": 5}
+    mode = sys.argv[1] if len(sys.argv) > 1 else ""
+    if mode not in nargs or len(sys.argv) < 2 + nargs[mode]:
+        print(__doc__.strip())
+        sys.exit(2)
     if mode == "traffic":
         print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5].split("\n")))
     elif mode == "sparseio":  # <dir> <workload,workload,...> <copy MiB> <LDS KiB> <commands>
