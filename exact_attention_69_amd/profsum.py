@@ -3,6 +3,7 @@
 usage: python -m exact_attention_69_amd.profsum stats <run_kernel_stats.csv> "<command>"
        python -m exact_attention_69_amd.profsum pmc <dir with p*/run_counter_collection.csv> "<command>"
        python -m exact_attention_69_amd.profsum traffic <dir> <workload> <copy MiB> "<commands>"
+       python -m exact_attention_69_amd.profsum sparseio <dir> <workload,...> <copy MiB> <LDS KiB> "<commands>"
 
 `traffic` reads <dir>/kt/run_kernel_stats.csv (a --kernel-trace --stats run)
 and <dir>/p*/run_counter_collection.csv (counter passes over the same
