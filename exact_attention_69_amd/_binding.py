@@ -167,6 +167,22 @@ def _check_gqa(q, k, v, *qlike):
     return Hkv
 
 
+def _out(t, shape, dtype, device):
+    """An output tensor: allocated when t is None; otherwise it must be a
+    contiguous GPU tensor of exactly this shape and dtype on this device,
+    since the kernels write every element of the shape they are given."""
+    torch = _torch()
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if (not t.is_cuda or t.device != torch.device(device) or tuple(t.shape) != shape or t.dtype != dtype
+            or not t.is_contiguous()):
+        raise ValueError(f"output must be a contiguous {dtype} GPU tensor of shape {shape} on {device}; got "
+                         f"shape {tuple(t.shape)}, {t.dtype}, on {t.device}"
+                         + ("" if t.is_contiguous() else ", not contiguous"))
+    return t
+
+
 def _call(fn, *args):
     with _torch().cuda.device(args[-1][0]):
         st = getattr(load_library(), fn)(*args[:-1], args[-1][1])
@@ -207,8 +223,8 @@ def attn_fwd(q, k, v, scale=None, window=-1, out=None, lse=None, stream=None):
     _check_inputs(q, k, v)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, q.dtype, q.device)
+    lse = _out(lse, (B, H, n), torch.float32, q.device)
     with torch.cuda.device(q.device):
         st = load_library().attn_fwd(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      scale, int(window), out.data_ptr(), lse.data_ptr(), _stream_ptr(q, stream))
@@ -240,9 +256,9 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None
     need = attn_bwd_workspace_bytes(code, B, H, n, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dq = _out(dq, q.shape, q.dtype, q.device)
+    dk = _out(dk, q.shape, q.dtype, q.device)
+    dv = _out(dv, q.shape, q.dtype, q.device)
     with torch.cuda.device(q.device):
         st = load_library().attn_bwd(code, B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                      do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(),
@@ -263,9 +279,9 @@ def attn_bwd_noalloc(q, k, v, o, do, lse, scale=None, window=-1, dq=None, dk=Non
     _check_lse(lse, q)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dq = _out(dq, q.shape, q.dtype, q.device)
+    dk = _out(dk, q.shape, q.dtype, q.device)
+    dv = _out(dv, q.shape, q.dtype, q.device)
     _call("attn_bwd_noalloc", _dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
           do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
           (q.device, _stream_ptr(q, stream)))
@@ -307,8 +323,8 @@ def attn_bwd_dkdv(q, k, v, do, lse, workspace, scale=None, window=-1, dk=None, d
     _check_lse(lse, q)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dk = _out(dk, q.shape, q.dtype, q.device)
+    dv = _out(dv, q.shape, q.dtype, q.device)
     with torch.cuda.device(q.device):
         st = load_library().attn_bwd_dkdv(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                           do.data_ptr(), lse.data_ptr(), scale, int(window), dk.data_ptr(),
@@ -327,7 +343,7 @@ def attn_bwd_dq(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, str
     _check_lse(lse, q)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
+    dq = _out(dq, q.shape, q.dtype, q.device)
     with torch.cuda.device(q.device):
         st = load_library().attn_bwd_dq(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                         do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(),
@@ -350,8 +366,8 @@ def attn_fwd_gqa(q, k, v, scale=None, window=-1, out=None, lse=None, stream=None
     Hkv = _check_gqa(q, k, v)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, q.dtype, q.device)
+    lse = _out(lse, (B, H, n), torch.float32, q.device)
     _call("attn_fwd_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale,
           int(window), out.data_ptr(), lse.data_ptr(), (q.device, _stream_ptr(q, stream)))
     return out, lse
@@ -369,9 +385,9 @@ def attn_bwd_gqa(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     workspace, wsb = _workspace(q, code, workspace)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = _out(dq, q.shape, q.dtype, q.device)
+    dk = _out(dk, k.shape, k.dtype, k.device)
+    dv = _out(dv, v.shape, v.dtype, v.device)
     _call("attn_bwd_gqa", code, B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
           do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
           workspace.data_ptr(), wsb, (q.device, _stream_ptr(q, stream)))
@@ -386,8 +402,8 @@ def attn_bwd_dkdv_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dk=Non
     _check_lse(lse, q)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dk = _out(dk, k.shape, k.dtype, k.device)
+    dv = _out(dv, v.shape, v.dtype, v.device)
     _call("attn_bwd_dkdv_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
           do.data_ptr(), lse.data_ptr(), scale, int(window), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
           workspace.numel() * workspace.element_size(), (q.device, _stream_ptr(q, stream)))
@@ -402,7 +418,7 @@ def attn_bwd_dq_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None,
     _check_lse(lse, q)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
+    dq = _out(dq, q.shape, q.dtype, q.device)
     _call("attn_bwd_dq_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
           do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), workspace.data_ptr(),
           workspace.numel() * workspace.element_size(), (q.device, _stream_ptr(q, stream)))
@@ -433,8 +449,8 @@ def attn_fwd_pattern(q, k, v, pattern, scale=None, out=None, lse=None, workspace
     _check_inputs(q, k, v)
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, q.dtype, q.device)
+    lse = _out(lse, (B, H, n), torch.float32, q.device)
     workspace, wsb = _pattern_workspace(q, workspace)
     pc = pattern.as_c(n, q.device)
     _call("attn_fwd_pattern", _dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale,
@@ -453,9 +469,9 @@ def attn_bwd_pattern(q, k, v, o, do, lse, pattern, scale=None, workspace=None, d
     B, H, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     workspace, wsb = _pattern_workspace(q, workspace)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = _out(dq, q.shape, q.dtype, q.device)
+    dk = _out(dk, k.shape, k.dtype, k.device)
+    dv = _out(dv, v.shape, v.dtype, v.device)
     pc = pattern.as_c(n, q.device)
     _call("attn_bwd_pattern", _dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
           do.data_ptr(), lse.data_ptr(), scale, ctypes.byref(pc), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
@@ -497,8 +513,8 @@ def attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, shape, scale=None, rota
     torch = _torch()
     B, H, n, d = shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty((B, H, n, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
-    lse = torch.empty((B, H, n), dtype=torch.float32, device=q8.device) if lse is None else lse
+    out = _out(out, (B, H, n, d), torch.bfloat16, q8.device)
+    lse = _out(lse, (B, H, n), torch.float32, q8.device)
     for t, lay in ((q8, EXATTN_FP8_ROWS), (k8, EXATTN_FP8_ROWS), (v8t, EXATTN_FP8_V_TRANSPOSED)):
         if t.dtype != torch.uint8 or not t.is_cuda or t.numel() < attn_fp8_bytes(B, H, n, d, lay):
             raise ValueError("FP8 inputs must be uint8 GPU tensors of attn_fp8_bytes() bytes")

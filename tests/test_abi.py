@@ -251,6 +251,15 @@ def test_binding_rejects_host_tensors():
         ea.attn_fwd(x, x, x)
 
 
+def test_binding_rejects_host_output_tensors():
+    """A caller-provided output must be a GPU tensor of the exact shape and
+    dtype (the kernels write every element of the shape they are given)."""
+    torch = pytest.importorskip("torch")
+    from exact_attention_69_amd import _binding as b
+    with pytest.raises(ValueError):
+        b._out(torch.zeros(1, 1, 8, 64), (1, 1, 8, 64), torch.float32, "cuda:0")
+
+
 def test_noalloc_backward_rejects_before_any_hip_call(lib):
     """attn_bwd_noalloc validates like attn_bwd and refuses problems whose
     row arrays exceed its fixed scratch buffer (the header's

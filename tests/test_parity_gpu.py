@@ -301,6 +301,31 @@ def test_windowed_backward_on_two_streams_stays_ordered_on_its_stream(d, Hkv):
     assert not torch.equal(got[0][0], got[1][0])
 
 
+def test_binding_checks_caller_outputs():
+    """Outputs handed to the binding must have the exact shape, dtype and
+    layout of the ones it would allocate; a wrong one is refused before any
+    launch, and a right one receives the same bits as an allocated one."""
+    import torch
+    import exact_attention_69_amd as ea
+    g = torch.Generator().manual_seed(3)
+    q, k, v, do = (torch.randn(1, 2, 100, 64, generator=g).bfloat16().cuda() for _ in range(4))
+    o, lse = ea.attn_fwd(q, k, v)
+    bad = [dict(out=torch.empty(1, 2, 99, 64, dtype=torch.bfloat16, device="cuda")),
+           dict(out=torch.empty(1, 2, 100, 64, dtype=torch.float32, device="cuda")),
+           dict(lse=torch.empty(1, 2, 100, dtype=torch.bfloat16, device="cuda")),
+           dict(out=torch.empty(1, 2, 64, 100, dtype=torch.bfloat16, device="cuda").transpose(2, 3))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            ea.attn_fwd(q, k, v, **kw)
+    with pytest.raises(ValueError):
+        ea.attn_bwd(q, k, v, o, do, lse, dk=torch.empty(1, 2, 100, 32, dtype=torch.bfloat16, device="cuda"))
+    o2 = torch.empty_like(q)
+    lse2 = torch.empty_like(lse)
+    ea.attn_fwd(q, k, v, out=o2, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 def test_windowed_backward_from_two_threads():
     """Two host threads, each with its own stream and inputs, call the
     windowed attn_bwd (whose dK/dV stage goes to the device's shared second
