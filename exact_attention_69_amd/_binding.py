@@ -263,7 +263,7 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, window=-1, workspace=None, dq=None
         st = load_library().attn_bwd(code, B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                      do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(),
                                      dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), _stream_ptr(q, stream))
+                                     _ws_bytes(workspace, q.device), _stream_ptr(q, stream))
     if st != 0:
         raise ExattnError("attn_bwd", st, exattn_status_string(st))
     return dq, dk, dv
@@ -288,13 +288,23 @@ def attn_bwd_noalloc(q, k, v, o, do, lse, scale=None, window=-1, dq=None, dk=Non
     return dq, dk, dv
 
 
+def _ws_bytes(workspace, device):
+    """Size in bytes of a caller's workspace, which must be a contiguous GPU
+    tensor on the problem's device (the library checks the size)."""
+    torch = _torch()
+    if not workspace.is_cuda or workspace.device != torch.device(device) or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous GPU tensor on {device}; got one on {workspace.device}"
+                         + ("" if workspace.is_contiguous() else ", not contiguous"))
+    return workspace.numel() * workspace.element_size()
+
+
 def _workspace(q, code, workspace):
     torch = _torch()
     B, H, n, d = q.shape
     need = attn_bwd_workspace_bytes(code, B, H, n, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    return workspace, workspace.numel() * workspace.element_size()
+    return workspace, _ws_bytes(workspace, q.device)
 
 
 @_on_call_stream
@@ -329,7 +339,7 @@ def attn_bwd_dkdv(q, k, v, do, lse, workspace, scale=None, window=-1, dk=None, d
         st = load_library().attn_bwd_dkdv(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                           do.data_ptr(), lse.data_ptr(), scale, int(window), dk.data_ptr(),
                                           dv.data_ptr(), workspace.data_ptr(),
-                                          workspace.numel() * workspace.element_size(), _stream_ptr(q, stream))
+                                          _ws_bytes(workspace, q.device), _stream_ptr(q, stream))
     if st != 0:
         raise ExattnError("attn_bwd_dkdv", st, exattn_status_string(st))
     return dk, dv
@@ -347,7 +357,7 @@ def attn_bwd_dq(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None, str
     with torch.cuda.device(q.device):
         st = load_library().attn_bwd_dq(_dtype_code(q), B, H, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                         do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(),
-                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        workspace.data_ptr(), _ws_bytes(workspace, q.device),
                                         _stream_ptr(q, stream))
     if st != 0:
         raise ExattnError("attn_bwd_dq", st, exattn_status_string(st))
@@ -406,7 +416,7 @@ def attn_bwd_dkdv_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dk=Non
     dv = _out(dv, v.shape, v.dtype, v.device)
     _call("attn_bwd_dkdv_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
           do.data_ptr(), lse.data_ptr(), scale, int(window), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-          workspace.numel() * workspace.element_size(), (q.device, _stream_ptr(q, stream)))
+          _ws_bytes(workspace, q.device), (q.device, _stream_ptr(q, stream)))
     return dk, dv
 
 
@@ -421,7 +431,7 @@ def attn_bwd_dq_gqa(q, k, v, do, lse, workspace, scale=None, window=-1, dq=None,
     dq = _out(dq, q.shape, q.dtype, q.device)
     _call("attn_bwd_dq_gqa", _dtype_code(q), B, H, Hkv, n, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
           do.data_ptr(), lse.data_ptr(), scale, int(window), dq.data_ptr(), workspace.data_ptr(),
-          workspace.numel() * workspace.element_size(), (q.device, _stream_ptr(q, stream)))
+          _ws_bytes(workspace, q.device), (q.device, _stream_ptr(q, stream)))
     return dq
 
 
@@ -439,7 +449,7 @@ def _pattern_workspace(q, workspace):
     need = attn_pattern_workspace_bytes(_dtype_code(q), B, H, n, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    return workspace, workspace.numel() * workspace.element_size()
+    return workspace, _ws_bytes(workspace, q.device)
 
 
 @_on_call_stream

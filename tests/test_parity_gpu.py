@@ -319,6 +319,11 @@ def test_binding_checks_caller_outputs():
             ea.attn_fwd(q, k, v, **kw)
     with pytest.raises(ValueError):
         ea.attn_bwd(q, k, v, o, do, lse, dk=torch.empty(1, 2, 100, 32, dtype=torch.bfloat16, device="cuda"))
+    # a workspace in host memory, or a strided one, is refused as well
+    with pytest.raises(ValueError):
+        ea.attn_bwd(q, k, v, o, do, lse, workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ea.attn_bwd_rowdot(o, do, lse, workspace=torch.empty(2, 1 << 16, dtype=torch.uint8, device="cuda")[:, ::2])
     o2 = torch.empty_like(q)
     lse2 = torch.empty_like(lse)
     ea.attn_fwd(q, k, v, out=o2, lse=lse2)
