@@ -506,8 +506,9 @@ def attn_quant_fp8(x, signs=None, layout=EXATTN_FP8_ROWS, stream=None):
     if x.dtype != torch.bfloat16:
         raise TypeError("attn_quant_fp8 takes bfloat16 input")
     B, H, n, d = x.shape
-    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d or not signs.is_cuda):
-        raise ValueError("signs must be a float32 GPU tensor of d entries (+1 or -1)")
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d or not signs.is_cuda
+                              or signs.device != x.device or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 tensor of d entries (+1 or -1) on x's GPU")
     x8 = torch.empty(max(attn_fp8_bytes(B, H, n, d, layout), 1), dtype=torch.uint8, device=x.device)
     scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
     _call("attn_quant_fp8", B, H, n, d, x.data_ptr(), None if signs is None else signs.data_ptr(), int(layout),
@@ -526,11 +527,13 @@ def attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, shape, scale=None, rota
     out = _out(out, (B, H, n, d), torch.bfloat16, q8.device)
     lse = _out(lse, (B, H, n), torch.float32, q8.device)
     for t, lay in ((q8, EXATTN_FP8_ROWS), (k8, EXATTN_FP8_ROWS), (v8t, EXATTN_FP8_V_TRANSPOSED)):
-        if t.dtype != torch.uint8 or not t.is_cuda or t.numel() < attn_fp8_bytes(B, H, n, d, lay):
-            raise ValueError("FP8 inputs must be uint8 GPU tensors of attn_fp8_bytes() bytes")
+        if (t.dtype != torch.uint8 or not t.is_cuda or t.device != q8.device or not t.is_contiguous()
+                or t.numel() < attn_fp8_bytes(B, H, n, d, lay)):
+            raise ValueError("FP8 inputs must be contiguous uint8 tensors of attn_fp8_bytes() bytes on one GPU")
     for t in (q_scale, k_scale, v_scale):
-        if t.dtype != torch.float32 or t.numel() != B * H or not t.is_cuda:
-            raise ValueError("scales must be float32 GPU tensors of B*H entries")
+        if (t.dtype != torch.float32 or t.numel() != B * H or not t.is_cuda or t.device != q8.device
+                or not t.is_contiguous()):
+            raise ValueError("scales must be contiguous float32 tensors of B*H entries on the inputs' GPU")
     _call("attn_fwd_fp8", B, H, n, d, q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), q_scale.data_ptr(),
           k_scale.data_ptr(), v_scale.data_ptr(), scale, int(bool(rotated)), out.data_ptr(), lse.data_ptr(),
           (q8.device, _stream_ptr(q8, stream)))
