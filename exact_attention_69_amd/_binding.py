@@ -150,6 +150,8 @@ def _check_inputs(*ts):
             raise ValueError("tensors must be on the GPU")
         if t.shape != t0.shape or t.dtype != t0.dtype:
             raise ValueError("Q, K, V (and O, dO) must share shape and dtype")
+        if t.device != t0.device:
+            raise ValueError("all tensors of a call must be on one GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, n, d]")
 
@@ -240,8 +242,9 @@ def attn_bwd_workspace_bytes(dtype_code, B, H, n, d):
 def _check_lse(lse, q):
     torch = _torch()
     B, H, n, _ = q.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, n]")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous() or not lse.is_cuda
+            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, n] on the inputs' GPU")
 
 
 @_on_call_stream
